@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE Q4 FFN layer on one MI355X.
+
+One step = one prefill layer call on the T=2048 chunk (moe_route + moe_prefill:
+router logits, top-8, histogram/scan/scatter/block maps, gate/up grouped GEMM
+with SiLU*up, routed down GEMM, shared down + fixed-order combine), inputs
+resident in HBM, two distinct weight sets alternated so the weights stream
+from HBM.  After the timed prefill steps the batch-1 decode layer is measured
+on 40 distinct layers cycled for `--decode-steps` steps (one moe_decode call
+per layer, every call on one stream), and the CPU oracle is timed on a bounded
+sample of the prefill workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import dataclasses
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E peak (published)
+METRIC = "prefill MoE-layer tok/s @T=2048 (%MFMA peak); decode GB/s per layer (%HBM peak)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def q4_bytes(N, K):
+    """Bytes of one N x K group-64 affine 4-bit matrix: codes + bf16 scale + bf16 bias."""
+    return N * K // 2 + N * (K // 64) * 4
+
+
+class HipEvents:
+    """HIP events through the process's (torch's) HIP runtime."""
+
+    def __init__(self):
+        with open("/proc/self/maps") as f:
+            path = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})[0]
+        self.rt = C.CDLL(path)
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.pool = []
+
+    def make(self, n):
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            if self.rt.hipEventCreate(C.byref(arr, i * C.sizeof(C.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+        self.pool.append(arr)
+        return arr
+
+    def record(self, ev, stream):
+        self.rt.hipEventRecord(ev, stream)
+
+    def ms(self, a, b):
+        out = C.c_float()
+        if self.rt.hipEventElapsedTime(C.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for arr in self.pool:
+            for e in arr:
+                self.rt.hipEventDestroy(e)
+        self.pool = []
+
+
+def prefill_work(T, d, I, E, k, counts):
+    """Algorithmic flops and bytes of one prefill layer call, per kernel and total."""
+    touched = int((counts > 0).sum())
+    gu_w = (touched + 1) * 2 * q4_bytes(I, d)
+    dn_w = (touched + 1) * q4_bytes(d, I)
+    f_gu = 4 * T * k * d * I + 4 * T * d * I
+    f_dn_routed = 2 * T * k * I * d
+    f_dn_shared = 2 * T * I * d
+    x_b, y_b, h_b, hs_b = 2 * T * d, 2 * T * d, 2 * T * k * I, 2 * T * I
+    return {
+        "touched_experts": touched,
+        "flops": f_gu + f_dn_routed + f_dn_shared,
+        "bytes": gu_w + dn_w + 4 * d * E + x_b + y_b,
+        "gate_up": {"flops": f_gu, "bytes": gu_w + x_b + h_b + hs_b},
+        "down": {"flops": f_dn_routed,
+                 "bytes": touched * q4_bytes(d, I) + h_b + 2 * T * k * d},
+        "shared_down_combine": {"flops": f_dn_shared,
+                                "bytes": q4_bytes(d, I) + hs_b + 2 * T * k * d + y_b},
+    }
+
+
+def roofline(flops, nbytes, seconds):
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    if t_mfma >= t_hbm:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBPS, 4), "traffic": None}
+
+
+def bench_prefill(args, q4, torch, ev, stream):
+    from workloads import WORKLOADS, make_layer
+    w = WORKLOADS["prefill2048"]
+    log(f"generating two weight sets for {w.name} (T={w.T}, d={w.d}, I={w.inter}, E={w.n_experts}, k={w.top_k})")
+    L0, x = make_layer(w)
+    L1, _ = make_layer(dataclasses.replace(w, seed=w.seed + 100))
+    dev = torch.device("cuda:0")
+    layers = [q4.DeviceLayer.from_host(L, dev) for L in (L0, L1)]
+    del L0, L1
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    r = q4.DeviceRouting(w.T, w.n_experts, w.top_k, dev)
+    ws = q4.workspace(layers[0], w.T, dev)
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+    lib = q4._abi.lib()
+
+    def step(i, trace_route=None, trace_pre=None):
+        if trace_route is not None:
+            lib.moe_trace_events(C.cast(trace_route, C.c_void_p), 4)
+        q4.route(layers[i % 2], xd, routing=r)
+        if trace_pre is not None:
+            lib.moe_trace_events(C.cast(trace_pre, C.c_void_p), 4)
+        q4.prefill(layers[i % 2], xd, r, ws, y)
+        lib.moe_trace_events(None, 0)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev_r = [ev.make(4) for _ in range(K)]
+    ev_p = [ev.make(4) for _ in range(K)]
+    t = ev.make(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.record(t[0], stream)
+    for i in range(K):
+        step(args.warmup + i, ev_r[i], ev_p[i])
+    ev.record(t[1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev.ms(t[0], t[1]) / K
+    names_r = ["router_logits", "topk", "route_sort"]
+    names_p = ["gate_up", "down", "shared_down_combine"]
+    per = {n: 0.0 for n in names_r + names_p}
+    for i in range(K):
+        for j, n in enumerate(names_r):
+            per[n] += ev.ms(ev_r[i][j], ev_r[i][j + 1]) / K
+        for j, n in enumerate(names_p):
+            per[n] += ev.ms(ev_p[i][j], ev_p[i][j + 1]) / K
+    counts = r.counts.cpu().numpy()
+    work = prefill_work(w.T, w.d, w.inter, w.n_experts, w.top_k, counts)
+    sec = ms_step / 1e3
+    tflops = work["flops"] / sec / 1e12
+    log(f"prefill: {ms_step * 1e3:.1f} us/layer ({wall / K * 1e3:.1f} us wall), "
+        f"{tflops:.1f} TFLOP/s, per kernel (us): " +
+        ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
+    out = {
+        "workload": w, "ms_per_step": ms_step, "wall_ms_per_step": wall / K * 1e3,
+        "tok_s": w.T / sec, "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "gbps": work["bytes"] / sec / 1e9, "work": work, "kernel_us": {n: v * 1e3 for n, v in per.items()},
+    }
+    gu_sec = per["gate_up"] / 1e3
+    out["roofline"] = roofline(work["gate_up"]["flops"], work["gate_up"]["bytes"], gu_sec)
+    out["roofline"]["kernel"] = "expert_gemm_kernel<4,0> (gate/up grouped GEMM + SiLU*up)"
+    out["roofline"]["mfma_frac"] = round(work["gate_up"]["flops"] / gu_sec / 1e12 / PEAK_BF16_TFLOPS, 4)
+    del layers, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(args, q4, torch, ev, stream):
+    from workloads import WORKLOADS, decode_inputs, make_layer
+    w = WORKLOADS["decode"]
+    n_layers, n_steps = args.decode_layers, args.decode_steps
+    dev = torch.device("cuda:0")
+    log(f"generating {n_layers} decode layers (d={w.d}, I={w.inter}, E={w.n_experts}, k={w.top_k})")
+    layers = []
+    for li in range(n_layers):
+        L, _ = make_layer(w, li)
+        layers.append(q4.DeviceLayer.from_host(L, dev))
+        del L
+    xs = torch.from_numpy(decode_inputs(w, n_steps).view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = q4.workspace(layers[0], 1, dev)
+    y = torch.empty((1, w.d), dtype=torch.bfloat16, device=dev)
+    lib = q4._abi.lib()
+    for li in range(n_layers):  # warm-up: one pass over all layers
+        q4.decode(layers[li], xs[0:1], ws, y)
+    torch.cuda.synchronize()
+    mid = n_steps // 2
+    ev_d = [ev.make(4) for _ in range(n_layers)]
+    t = ev.make(2)
+    ev.record(t[0], stream)
+    for st in range(n_steps):
+        for li in range(n_layers):
+            if st == mid:
+                lib.moe_trace_events(C.cast(ev_d[li], C.c_void_p), 4)
+            q4.decode(layers[li], xs[st:st + 1], ws, y)
+            if st == mid:
+                lib.moe_trace_events(None, 0)
+    ev.record(t[1], stream)
+    torch.cuda.synchronize()
+    calls = n_steps * n_layers
+    us_layer = ev.ms(t[0], t[1]) * 1e3 / calls
+    names = ["router", "gate_up", "down"]
+    per = {n: sum(ev.ms(ev_d[li][j], ev_d[li][j + 1]) for li in range(n_layers)) * 1e3 / n_layers
+           for j, n in enumerate(names)}
+    expert_bytes = (w.top_k + 1) * (2 * q4_bytes(w.inter, w.d) + q4_bytes(w.d, w.inter))
+    router_bytes = 4 * w.d * w.n_experts
+    gbps = expert_bytes / (us_layer * 1e-6) / 1e9
+    log(f"decode eager: {us_layer:.2f} us/layer, {gbps:.0f} GB/s on the 9 experts' bytes, "
+        f"per kernel (us): " + ", ".join(f"{n}={v:.2f}" for n, v in per.items()))
+    out = {"us_per_layer": us_layer, "gbps": gbps, "hbm_frac": gbps / PEAK_HBM_GBPS,
+           "gbps_incl_router": (expert_bytes + router_bytes) / (us_layer * 1e-6) / 1e9,
+           "expert_bytes_per_layer": expert_bytes, "kernel_us": per,
+           "layers": n_layers, "steps": n_steps, "calls": calls}
+    # the same 40-layer step captured once in a HIP graph and replayed
+    if not args.no_graph:
+        y_eager = y.clone()
+        g = torch.cuda.CUDAGraph()
+        gx = xs[n_steps - 1:n_steps].clone()
+        with torch.cuda.graph(g):
+            for li in range(n_layers):
+                q4.decode(layers[li], gx, ws, y)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y, y_eager))
+        reps = max(1, n_steps // 4)
+        t2 = ev.make(2)
+        gs = torch.cuda.current_stream()
+        ev.record(t2[0], int(gs.cuda_stream))
+        for _ in range(reps):
+            g.replay()
+        ev.record(t2[1], int(gs.cuda_stream))
+        torch.cuda.synchronize()
+        us_g = ev.ms(t2[0], t2[1]) * 1e3 / (reps * n_layers)
+        out["graph"] = {"us_per_layer": us_g, "gbps": expert_bytes / (us_g * 1e-6) / 1e9,
+                        "hbm_frac": expert_bytes / (us_g * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                        "replays": reps, "matches_eager": same}
+        log(f"decode graph: {us_g:.2f} us/layer ({out['graph']['gbps']:.0f} GB/s), "
+            f"output equal to eager: {same}")
+        del g
+    ex_bytes = expert_bytes
+    k_sec = sum(per.values()) / 1e6
+    out["roofline"] = {"bound": "hbm", "achieved": round(ex_bytes / k_sec / 1e9, 1),
+                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                       "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
+                       "kernels": "decode_router + decode_gate_up + decode_down"}
+    del layers, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(n_tokens):
+    import oracle
+    from workloads import WORKLOADS, make_layer
+    w = WORKLOADS["prefill2048"]
+    L, x = make_layer(w)
+    xs = x[:n_tokens]
+    t0 = time.perf_counter()
+    logits = oracle.router_logits(xs, L["w_router"], L["router_bias"])
+    r = oracle.route(logits, w.top_k)
+    oracle.layer_tokens(L, xs, np.arange(n_tokens, dtype=np.int32), r["idx"], r["w"])
+    sec = time.perf_counter() - t0
+    return {"value": round(n_tokens / sec, 3), "unit": "tok/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"first {n_tokens} tokens of the prefill T=2048 layer: router logits, "
+                      f"routing and all {w.top_k}+1 expert FFNs of those tokens (fp64 oracle)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-layers", type=int, default=40)
+    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this layer build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import q4_routed_expert_amd as q4
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ev = HipEvents()
+    stream = int(torch.cuda.current_stream().cuda_stream)
+    pre = bench_prefill(args, q4, torch, ev, stream)
+    dec = None if args.no_decode else bench_decode(args, q4, torch, ev, stream)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
+    ev.close()
+    w = pre["workload"]
+    line = {
+        "metric": METRIC, "value": round(pre["tok_s"], 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"routed-MoE FFN layer, prefill chunk T={w.T}, d={w.d}, "
+                               f"I={w.inter}, E={w.n_experts}, top-{w.top_k} + 1 shared expert, "
+                               f"Q4 group-64 weights (bf16 scale/bias), 2 weight sets alternated",
+                   "T": w.T, "d": w.d, "inter": w.inter, "n_experts": w.n_experts,
+                   "top_k": w.top_k, "seed": w.seed},
+        "us_per_layer": round(pre["ms_per_step"] * 1e3, 2),
+        "tflops": round(pre["tflops"], 2), "mfma_frac": round(pre["mfma_frac"], 4),
+        "gbps": round(pre["gbps"], 1), "hbm_frac": round(pre["gbps"] / PEAK_HBM_GBPS, 4),
+        "kernel_us": {n: round(v, 2) for n, v in pre["kernel_us"].items()},
+        "algorithmic": {"flops": pre["work"]["flops"], "bytes": pre["work"]["bytes"],
+                        "touched_experts": pre["work"]["touched_experts"]},
+        "roofline": pre["roofline"],
+    }
+    if dec is not None:
+        line["decode"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in dec.items()
+                          if k not in ("roofline", "graph", "kernel_us")}
+        line["decode"]["kernel_us"] = {n: round(v, 3) for n, v in dec["kernel_us"].items()}
+        if "graph" in dec:
+            line["decode"]["graph"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                       for k, v in dec["graph"].items()}
+        line["roofline_decode"] = dec["roofline"]
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

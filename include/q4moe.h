@@ -1,0 +1,192 @@
+/*
+ * q4moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts FFN layer
+ * with group-64 affine 4-bit expert weights.
+ *
+ * Sources.  [Lily-M5] is the page "Perplexity's Lily beats MLX-LM on MacBook
+ * M5 because it only runs one model"; sections are named in quotes.
+ *   - "Why Qwen3.6-35B-A3B is a weird workload": a router scores the experts,
+ *     picks 8 of 256, and adds one shared expert that sees every token.
+ *   - "Prefill: keep routing on the GPU, dequantize in flight": weights are
+ *     groupwise affine 4-bit, each group of 64 sharing a bf16 scale and bias
+ *     (w = q * scale + bias); the grouped GEMM dequantises one tile at a time
+ *     on chip, accumulates in FP32, writes bf16 and never materialises the
+ *     expanded weights; routing (histogram, prefix scan, scatter, block map)
+ *     runs on the GPU inside the chunk's command stream with no CPU round
+ *     trip; tiles of 32 rows.
+ *   - "Decode: minimize bytes per token": batch-1 expert projections are
+ *     bandwidth-bound matrix-vector products; expert input projections are
+ *     fused with the gate activation, and the output projection with the
+ *     routing scores and the shared expert.
+ *   - "Setup": the runtime rejects any checkpoint that is not exactly the
+ *     supported architecture and quantisation.  Every entry point here is
+ *     likewise fail-closed: an unsupported shape is refused before anything
+ *     is enqueued.
+ *
+ * What the layer computes, per token t with input x_t (bf16, length d):
+ *   l_t    = x_t . W_r (+ b_r)                 fp32 router logits, E experts
+ *   idx_t  = the k experts with the largest l_t, larger logit first, equal
+ *            logits ordered by lower expert index
+ *   w_t    = softmax(l_t) at idx_t, divided by its sum over the k slots
+ *   E_e(x) = W_down,e . bf16( SiLU(W_gate,e . x) * (W_up,e . x) )
+ *   y_t    = bf16( sum_{s=0..k-1} w_t[s] * E_idx_t[s](x_t)  +  E_shared(x_t) )
+ * with the k routed terms added in slot order and the shared expert last,
+ * every weight used as the bf16 value bf16(q * scale + bias), and all sums
+ * accumulated in fp32.
+ *
+ * Conventions for every entry point.
+ *   - All array arguments are DEVICE pointers owned by the caller, 16-byte
+ *     aligned.  bf16 and fp16 values are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued on it: no entry point allocates, frees, copies to the host or
+ *     synchronises.  A return of MOE_OK means "validated and enqueued"; a
+ *     device fault surfaces at the caller's next synchronisation.
+ *   - Validation happens on the host before any launch; on any error nothing
+ *     is enqueued.  moe_last_error() then returns a one-line reason (kept per
+ *     host thread).
+ *   - Calls that share a workspace or routing buffers must not overlap
+ *     (run them on one stream, or order the streams).
+ */
+#ifndef Q4MOE_H
+#define Q4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* null or misaligned pointer, non-positive size */
+    MOE_EUNSUPPORTED = -2, /* shape outside what the kernels support (see limits) */
+    MOE_EWORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes() */
+    MOE_EHIP = -4          /* a HIP launch reported an error */
+};
+
+/* Limits of the kernels.  d and inter must also be multiples of 64 (the
+   quantisation group) and 1 <= top_k <= min(MOE_MAX_TOPK, n_experts). */
+#define MOE_GROUP 64
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+#define MOE_MAX_TOKENS 32768
+#define MOE_MAX_D 8192
+#define MOE_MAX_INTER 2048
+
+/* Row heights of the two block maps moe_route writes: the 32-row tile map
+   that describes the expert-sorted rows, and the 128-row work map the grouped
+   GEMMs walk (one work item = up to four 32-row tiles of one expert, so that a
+   dequantised weight tile is reused across them). */
+#define MOE_BLOCK_ROWS 32
+#define MOE_TILE_ROWS 128
+
+/* moe_route flag: start from the logits already in routing->logits instead of
+   computing them (used to route from given fp32 logits). */
+#define MOE_LOGITS_IN 1u
+
+/* One stack of group-64 affine 4-bit matrices, each N rows by K columns:
+     q     [n_mat][N][K/8]  uint32, eight 4-bit codes per word along K, the
+                            lowest nibble holding the lowest k
+     scale [n_mat][N][K/64] bf16
+     bias  [n_mat][N][K/64] bf16
+   Row n of matrix m holds the weights that produce output n from the K
+   inputs; w(n, k) = q(n, k) * scale(n, k/64) + bias(n, k/64). */
+typedef struct {
+    const uint32_t* q;
+    const uint16_t* scale;
+    const uint16_t* bias;
+} moe_q4mat;
+
+/* One MoE layer.  Routed experts: gate and up are n_experts matrices of
+   inter x d, down is n_experts matrices of d x inter.  The shared expert's
+   sh_gate, sh_up (inter x d) and sh_down (d x inter) are single matrices. */
+typedef struct {
+    int32_t d;               /* hidden size */
+    int32_t inter;           /* expert intermediate size (shared expert too) */
+    int32_t n_experts;       /* E, routed experts */
+    int32_t top_k;           /* k */
+    const float* w_router;   /* fp32 [d][E], row-major */
+    const float* router_bias;/* fp32 [E], added to the logits; may be NULL */
+    moe_q4mat gate, up, down;
+    moe_q4mat sh_gate, sh_up, sh_down;
+} moe_layer;
+
+/* Routing state of one chunk of T tokens, all device arrays owned by the
+   caller.  Written by moe_route (logits are read instead when MOE_LOGITS_IN is
+   set) and read by moe_prefill.  An "assignment" is a = t*k + s (token t,
+   slot s); the "sorted rows" are the assignments grouped by expert (experts
+   ascending, tokens ascending inside an expert). */
+typedef struct {
+    float* logits;      /* [T][E]  fp32 router logits */
+    int32_t* topk_idx;  /* [T][k]  selected experts, slot 0 = largest logit */
+    float* topk_w;      /* [T][k]  renormalised scores */
+    int32_t* counts;    /* [E]     assignments per expert */
+    int32_t* offsets;   /* [E+1]   exclusive prefix sum of counts */
+    int32_t* perm;      /* [T*k]   sorted row -> assignment */
+    int32_t* inv_perm;  /* [T*k]   assignment -> sorted row */
+    int32_t* block_map; /* [T*k/32 + E][2]  (expert, first sorted row) per 32-row tile */
+    int32_t* n_blocks;  /* [1] */
+    int32_t* tile_map;  /* [T*k/128 + E][2] (expert, first sorted row) per 128-row item */
+    int32_t* n_tiles;   /* [1] */
+} moe_routing;
+
+/* Entries needed in block_map / tile_map for T tokens (pairs of int32). */
+int32_t moe_block_map_capacity(int32_t T, int32_t top_k, int32_t n_experts, int32_t rows);
+
+/* Bytes of device workspace moe_prefill (T tokens) and moe_decode (T = 1)
+   need for this layer shape: the gate/up activations h (bf16), the shared
+   expert's activations, the routed experts' fp16 outputs before the combine,
+   and the decode path's router partial sums.  0 on invalid arguments.  The
+   workspace must be zero-filled once before its first use by moe_decode
+   (moe_decode leaves its counter at zero again on exit). */
+size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
+
+/* Routing of T tokens, entirely on the device, no host synchronisation:
+   router logits (unless MOE_LOGITS_IN), top-k selection and renormalised
+   scores, histogram, exclusive scan, stable scatter into expert-sorted order,
+   and both block maps.  x: bf16 [T][d].  ([Lily-M5] "Prefill: keep routing on
+   the GPU, dequantize in flight".) */
+int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+              const moe_routing* r, void* stream);
+
+/* The expert part of the layer for T tokens routed by moe_route: grouped
+   gate/up GEMM with fused SiLU(gate)*up over the expert-sorted rows plus the
+   shared expert over all tokens, then the down projection of the routed rows,
+   then the shared expert's down projection fused with the fixed-order combine
+   (slots in order, scores applied, shared expert last).  Dequantisation
+   happens on chip, tile by tile; accumulation is fp32; y: bf16 [T][d].
+   ws must hold moe_workspace_bytes(L, T) bytes. */
+int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r,
+                void* ws, size_t ws_bytes, uint16_t* y, void* stream);
+
+/* The whole layer for one token (T = 1): router, top-k, then dequant-GEMVs
+   over the k selected experts and the shared expert with SiLU(gate)*up fused,
+   then the down GEMVs fused with the scores, the shared expert and the
+   combine.  r may be NULL; when given, r->logits [1][E], r->topk_idx [1][k]
+   and r->topk_w [1][k] are written (with MOE_LOGITS_IN, r->logits is read
+   and the router is skipped).  x, y: bf16 [1][d].  ([Lily-M5] "Decode:
+   minimize bytes per token".) */
+int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_routing* r,
+               void* ws, size_t ws_bytes, uint16_t* y, void* stream);
+
+/* The on-chip dequantisation the GEMMs use, exposed for testing: w_out (bf16
+   [n_rows][K]) = bf16(q * scale + bias) for matrix 0 of m.  K % 64 == 0. */
+int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, void* stream);
+
+/* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill and
+   moe_decode call made on this host thread records events[0] on its stream
+   before its first kernel and events[i] right after its i-th kernel, for
+   i < n (moe_route: 3 kernels, 2 with MOE_LOGITS_IN; moe_prefill: gate/up,
+   down, shared down + combine; moe_decode: router, gate/up, down).  The
+   elapsed time between consecutive events is one kernel's duration.  events
+   are hipEvent_t handles created and owned by the caller; pass NULL to stop. */
+void moe_trace_events(void* const* events, int32_t n);
+
+/* Text for a status code, and the reason for the last failure on this thread. */
+const char* moe_strerror(int code);
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4MOE_H */

@@ -138,14 +138,20 @@ static oracle_q4 expert_matrix(oracle_q4 m, int64_t e, int64_t N, int64_t K) {
 /* O2: l[t][e] = fp32( sum_j x[t][j] * W_r[j][e]  (+ b[e]) ) */
 void oracle_router_logits(const uint16_t* x, int64_t T, int64_t d, const float* w_router,
                           const float* router_bias, int64_t E, float* logits) {
-    for (int64_t t = 0; t < T; ++t)
-        for (int64_t e = 0; e < E; ++e) {
-            double acc = 0.0;
-            for (int64_t j = 0; j < d; ++j)
-                acc += bf16_value(x[t * d + j]) * (double)w_router[j * E + e];
-            if (router_bias) acc += (double)router_bias[e];
-            logits[t * E + e] = (float)acc;
+    double* acc = (double*)malloc(sizeof(double) * (size_t)E);
+    for (int64_t t = 0; t < T; ++t) {
+        /* every acc[e] still sums its terms j = 0, 1, ..., d-1 in order */
+        for (int64_t e = 0; e < E; ++e) acc[e] = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            const double xj = bf16_value(x[t * d + j]);
+            for (int64_t e = 0; e < E; ++e) acc[e] += xj * (double)w_router[j * E + e];
         }
+        for (int64_t e = 0; e < E; ++e) {
+            if (router_bias) acc[e] += (double)router_bias[e];
+            logits[t * E + e] = (float)acc[e];
+        }
+    }
+    free(acc);
 }
 
 /* O3-O7: selection, scores, histogram, exclusive scan, expert-sorted order. */

@@ -1,0 +1,297 @@
+// abi.hip -- the extern "C" entry points declared in include/q4moe.h:
+// host-side validation (fail-closed, nothing is enqueued on error), workspace
+// layout, and the launches on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+// Timing hook state (moe_trace_events): caller-owned events, next index.
+thread_local hipEvent_t* g_trace = nullptr;
+thread_local int g_trace_n = 0, g_trace_next = 0;
+
+void trace_begin(hipStream_t s) {
+    g_trace_next = 0;
+    q4moe::trace_point(s);
+}
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptr(const void* p, const char* what, bool allow_null = false) {
+    if (!p) return allow_null ? MOE_OK : fail(MOE_EINVAL, "%s is NULL", what);
+    if (!aligned16(p)) return fail(MOE_EINVAL, "%s is not 16-byte aligned", what);
+    return MOE_OK;
+}
+
+int check_mat(const moe_q4mat& m, const char* name) {
+    char buf[64];
+    int rc;
+    snprintf(buf, sizeof buf, "%s.q", name);
+    if ((rc = check_ptr(m.q, buf))) return rc;
+    snprintf(buf, sizeof buf, "%s.scale", name);
+    if ((rc = check_ptr(m.scale, buf))) return rc;
+    snprintf(buf, sizeof buf, "%s.bias", name);
+    return check_ptr(m.bias, buf);
+}
+
+int check_layer(const moe_layer* L) {
+    if (!L) return fail(MOE_EINVAL, "layer is NULL");
+    if (L->d <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k <= 0)
+        return fail(MOE_EINVAL, "non-positive layer size (d=%d inter=%d E=%d k=%d)", L->d,
+                    L->inter, L->n_experts, L->top_k);
+    if (L->d % MOE_GROUP || L->inter % MOE_GROUP)
+        return fail(MOE_EUNSUPPORTED, "d=%d and inter=%d must be multiples of %d", L->d,
+                    L->inter, MOE_GROUP);
+    if (L->d > MOE_MAX_D || L->inter > MOE_MAX_INTER)
+        return fail(MOE_EUNSUPPORTED, "d=%d > %d or inter=%d > %d", L->d, MOE_MAX_D, L->inter,
+                    MOE_MAX_INTER);
+    if (L->n_experts > MOE_MAX_EXPERTS)
+        return fail(MOE_EUNSUPPORTED, "n_experts=%d > %d", L->n_experts, MOE_MAX_EXPERTS);
+    if (L->top_k > MOE_MAX_TOPK || L->top_k > L->n_experts)
+        return fail(MOE_EUNSUPPORTED, "top_k=%d must be <= min(%d, n_experts=%d)", L->top_k,
+                    MOE_MAX_TOPK, L->n_experts);
+    int rc;
+    if ((rc = check_ptr(L->w_router, "w_router"))) return rc;
+    if ((rc = check_ptr(L->router_bias, "router_bias", true))) return rc;
+    if ((rc = check_mat(L->gate, "gate")) || (rc = check_mat(L->up, "up")) ||
+        (rc = check_mat(L->down, "down")) || (rc = check_mat(L->sh_gate, "sh_gate")) ||
+        (rc = check_mat(L->sh_up, "sh_up")) || (rc = check_mat(L->sh_down, "sh_down")))
+        return rc;
+    return MOE_OK;
+}
+
+int check_tokens(int32_t T) {
+    if (T <= 0) return fail(MOE_EINVAL, "T=%d must be positive", T);
+    if (T > MOE_MAX_TOKENS) return fail(MOE_EUNSUPPORTED, "T=%d > %d", T, MOE_MAX_TOKENS);
+    return MOE_OK;
+}
+
+int check_routing(const moe_routing* r) {
+    if (!r) return fail(MOE_EINVAL, "routing is NULL");
+    int rc;
+    if ((rc = check_ptr(r->logits, "routing.logits")) || (rc = check_ptr(r->topk_idx, "routing.topk_idx")) ||
+        (rc = check_ptr(r->topk_w, "routing.topk_w")) || (rc = check_ptr(r->counts, "routing.counts")) ||
+        (rc = check_ptr(r->offsets, "routing.offsets")) || (rc = check_ptr(r->perm, "routing.perm")) ||
+        (rc = check_ptr(r->inv_perm, "routing.inv_perm")) ||
+        (rc = check_ptr(r->block_map, "routing.block_map")) ||
+        (rc = check_ptr(r->n_blocks, "routing.n_blocks")) ||
+        (rc = check_ptr(r->tile_map, "routing.tile_map")) ||
+        (rc = check_ptr(r->n_tiles, "routing.n_tiles")))
+        return rc;
+    return MOE_OK;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace: [decode region | prefill region].  The decode region comes first
+// and prefill never writes it, so the decode arrival counter stays zero
+// between calls even when one workspace serves both.
+struct DecodeWs {
+    size_t counter, sel_idx, sel_w, logits, partial, h, total;
+};
+DecodeWs decode_ws(const moe_layer* L) {
+    DecodeWs w;
+    size_t o = 0;
+    w.counter = o; o += 256;
+    w.sel_idx = o; o += align256(sizeof(int32_t) * MOE_MAX_TOPK);
+    w.sel_w = o; o += align256(sizeof(float) * MOE_MAX_TOPK);
+    w.logits = o; o += align256(sizeof(float) * L->n_experts);
+    w.partial = o; o += align256(sizeof(float) * (size_t)(L->d / 32) * L->n_experts);
+    w.h = o; o += align256(sizeof(uint16_t) * (size_t)(L->top_k + 1) * L->inter);
+    w.total = o;
+    return w;
+}
+struct PrefillWs {
+    size_t h, h_sh, part, total;
+};
+PrefillWs prefill_ws(const moe_layer* L, int32_t T, size_t base) {
+    PrefillWs w;
+    const size_t A = (size_t)T * L->top_k;
+    size_t o = base;
+    w.h = o; o += align256(sizeof(uint16_t) * A * L->inter);
+    w.h_sh = o; o += align256(sizeof(uint16_t) * (size_t)T * L->inter);
+    w.part = o; o += align256(sizeof(uint16_t) * A * L->d);
+    w.total = o;
+    return w;
+}
+
+q4moe::Q4 q4(const moe_q4mat& m) { return q4moe::Q4{m.q, m.scale, m.bias}; }
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+}  // namespace
+
+namespace q4moe {
+void trace_point(hipStream_t s) {
+    if (g_trace && g_trace_next < g_trace_n) (void)hipEventRecord(g_trace[g_trace_next++], s);
+}
+}  // namespace q4moe
+
+extern "C" {
+
+void moe_trace_events(void* const* events, int32_t n) {
+    g_trace = (events && n > 0) ? (hipEvent_t*)events : nullptr;
+    g_trace_n = g_trace ? n : 0;
+    g_trace_next = 0;
+}
+
+int32_t moe_block_map_capacity(int32_t T, int32_t top_k, int32_t n_experts, int32_t rows) {
+    if (T <= 0 || top_k <= 0 || n_experts <= 0 || rows <= 0) return 0;
+    const int64_t A = (int64_t)T * top_k;
+    return (int32_t)(A / rows + (n_experts < A ? n_experts : A));
+}
+
+size_t moe_workspace_bytes(const moe_layer* L, int32_t T) {
+    if (check_layer(L) || check_tokens(T)) return 0;
+    const DecodeWs dw = decode_ws(L);
+    return prefill_ws(L, T, dw.total).total;
+}
+
+int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+              const moe_routing* r, void* stream) {
+    int rc;
+    if ((rc = check_layer(L)) || (rc = check_tokens(T)) || (rc = check_routing(r))) return rc;
+    const bool logits_in = flags & MOE_LOGITS_IN;
+    if (flags & ~MOE_LOGITS_IN) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+    if (!logits_in && (rc = check_ptr(x, "x"))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    trace_begin(s);
+    if (!logits_in &&
+        (rc = hip_status(q4moe::launch_router_logits(x, T, L->d, L->w_router, L->router_bias,
+                                                     L->n_experts, r->logits, s),
+                         "router logits")))
+        return rc;
+    if ((rc = hip_status(q4moe::launch_topk(r->logits, T, L->n_experts, L->top_k, r->topk_idx,
+                                            r->topk_w, s),
+                         "top-k")))
+        return rc;
+    return hip_status(q4moe::launch_route_sort(r->topk_idx, T, L->top_k, L->n_experts, r, s),
+                      "route sort");
+}
+
+int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r, void* ws,
+                size_t ws_bytes, uint16_t* y, void* stream) {
+    int rc;
+    if ((rc = check_layer(L)) || (rc = check_tokens(T)) || (rc = check_routing(r)) ||
+        (rc = check_ptr(x, "x")) || (rc = check_ptr(y, "y")) || (rc = check_ptr(ws, "workspace")))
+        return rc;
+    const size_t need = moe_workspace_bytes(L, T);
+    if (ws_bytes < need)
+        return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    const PrefillWs pw = prefill_ws(L, T, decode_ws(L).total);
+    unsigned char* base = (unsigned char*)ws;
+    q4moe::PrefillArgs a;
+    a.x = x;
+    a.T = T;
+    a.d = L->d;
+    a.I = L->inter;
+    a.E = L->n_experts;
+    a.k = L->top_k;
+    a.gate = q4(L->gate);
+    a.up = q4(L->up);
+    a.down = q4(L->down);
+    a.sh_gate = q4(L->sh_gate);
+    a.sh_up = q4(L->sh_up);
+    a.sh_down = q4(L->sh_down);
+    a.perm = r->perm;
+    a.offsets = r->offsets;
+    a.tile_map = r->tile_map;
+    a.n_tiles = r->n_tiles;
+    a.topk_w = r->topk_w;
+    a.tile_bound = moe_block_map_capacity(T, L->top_k, L->n_experts, MOE_TILE_ROWS);
+    a.h = (uint16_t*)(base + pw.h);
+    a.h_sh = (uint16_t*)(base + pw.h_sh);
+    a.part = (uint16_t*)(base + pw.part);
+    a.y = y;
+    trace_begin((hipStream_t)stream);
+    return hip_status(q4moe::launch_prefill(a, (hipStream_t)stream), "prefill");
+}
+
+int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_routing* r,
+               void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+    int rc;
+    if ((rc = check_layer(L)) || (rc = check_ptr(y, "y")) || (rc = check_ptr(ws, "workspace")))
+        return rc;
+    if (flags & ~MOE_LOGITS_IN) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+    const bool logits_in = flags & MOE_LOGITS_IN;
+    if ((rc = check_ptr(x, "x"))) return rc;
+    if (logits_in && (!r || !r->logits))
+        return fail(MOE_EINVAL, "MOE_LOGITS_IN needs routing->logits");
+    if (r) {
+        if ((rc = check_ptr(r->logits, "routing.logits", true)) ||
+            (rc = check_ptr(r->topk_idx, "routing.topk_idx", true)) ||
+            (rc = check_ptr(r->topk_w, "routing.topk_w", true)))
+            return rc;
+    }
+    const size_t need = moe_workspace_bytes(L, 1);
+    if (ws_bytes < need)
+        return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    const DecodeWs dw = decode_ws(L);
+    unsigned char* base = (unsigned char*)ws;
+    q4moe::DecodeArgs a;
+    a.x = x;
+    a.d = L->d;
+    a.I = L->inter;
+    a.E = L->n_experts;
+    a.k = L->top_k;
+    a.w_router = L->w_router;
+    a.router_bias = L->router_bias;
+    a.gate = q4(L->gate);
+    a.up = q4(L->up);
+    a.down = q4(L->down);
+    a.sh_gate = q4(L->sh_gate);
+    a.sh_up = q4(L->sh_up);
+    a.sh_down = q4(L->sh_down);
+    a.logits_in = logits_in;
+    a.logits = (r && r->logits) ? r->logits : (float*)(base + dw.logits);
+    a.out_idx = r ? r->topk_idx : nullptr;
+    a.out_w = r ? r->topk_w : nullptr;
+    a.partial = (float*)(base + dw.partial);
+    a.counter = (uint32_t*)(base + dw.counter);
+    a.sel_idx = (int32_t*)(base + dw.sel_idx);
+    a.sel_w = (float*)(base + dw.sel_w);
+    a.h = (uint16_t*)(base + dw.h);
+    a.y = y;
+    trace_begin((hipStream_t)stream);
+    return hip_status(q4moe::launch_decode(a, (hipStream_t)stream), "decode");
+}
+
+int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, void* stream) {
+    int rc;
+    if (!m) return fail(MOE_EINVAL, "matrix is NULL");
+    if ((rc = check_mat(*m, "m")) || (rc = check_ptr(w_out, "w_out"))) return rc;
+    if (n_rows <= 0 || K <= 0) return fail(MOE_EINVAL, "n_rows=%d K=%d", n_rows, K);
+    if (K % MOE_GROUP) return fail(MOE_EUNSUPPORTED, "K=%d not a multiple of %d", K, MOE_GROUP);
+    return hip_status(q4moe::launch_dequant(q4(*m), n_rows, K, w_out, (hipStream_t)stream),
+                      "dequant");
+}
+
+const char* moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_EUNSUPPORTED: return "unsupported shape";
+        case MOE_EWORKSPACE: return "workspace too small";
+        case MOE_EHIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+}  // extern "C"

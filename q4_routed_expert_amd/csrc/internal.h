@@ -1,0 +1,65 @@
+// internal.h -- launchers shared between the translation units of libq4moe.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "q4moe.h"
+#include "q4moe_dev.h"
+
+namespace q4moe {
+
+static_assert(kMaxExperts == MOE_MAX_EXPERTS && kMaxTopK == MOE_MAX_TOPK, "limits");
+static_assert(kBlockRows == MOE_BLOCK_ROWS && kTileRows == MOE_TILE_ROWS, "map rows");
+
+// Records the next event of the caller's timing hook (moe_trace_events) on s,
+// if one is installed on this host thread; called after every kernel launch.
+void trace_point(hipStream_t s);
+
+// Routing ([Lily-M5] "Prefill: keep routing on the GPU, dequantize in flight").
+hipError_t launch_router_logits(const uint16_t* x, int T, int d, const float* w_router,
+                                const float* router_bias, int E, float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t s);
+hipError_t launch_route_sort(const int32_t* idx, int T, int k, int E, const moe_routing* r,
+                             hipStream_t s);
+
+// Prefill expert GEMMs.
+struct PrefillArgs {
+    const uint16_t* x;
+    int T, d, I, E, k;
+    Q4 gate, up, down, sh_gate, sh_up, sh_down;
+    const int32_t* perm;
+    const int32_t* offsets;
+    const int32_t* tile_map;
+    const int32_t* n_tiles;
+    const float* topk_w;
+    int tile_bound;      // host upper bound on *n_tiles
+    uint16_t* h;         // bf16 [T*k][I], expert-sorted rows
+    uint16_t* h_sh;      // bf16 [T][I]
+    uint16_t* part;      // fp16 [T*k][d], rows in assignment order
+    uint16_t* y;         // bf16 [T][d]
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+// Decode (T = 1).
+struct DecodeArgs {
+    const uint16_t* x;
+    int d, I, E, k;
+    const float* w_router;
+    const float* router_bias;
+    Q4 gate, up, down, sh_gate, sh_up, sh_down;
+    bool logits_in;
+    float* logits;       // [E]: written, or read when logits_in
+    int32_t* out_idx;    // [k] or NULL
+    float* out_w;        // [k] or NULL
+    float* partial;      // [d/32][E] router partial sums
+    uint32_t* counter;   // arrival counter, zero between calls
+    int32_t* sel_idx;    // [k]
+    float* sel_w;        // [k]
+    uint16_t* h;         // bf16 [k+1][I]
+    uint16_t* y;         // bf16 [d]
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+hipError_t launch_dequant(Q4 m, int n_rows, int K, uint16_t* w_out, hipStream_t s);
+
+}  // namespace q4moe

@@ -1,0 +1,148 @@
+"""Host-side checks of the C-ABI library: it loads, exports every function the
+header declares, and refuses invalid arguments before touching the GPU.
+None of these calls launches a kernel, so they run without a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from q4_routed_expert_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4moe.h")
+
+# Nonzero, 16-byte aligned fake device addresses: validation only looks at them.
+FAKE = 0x10000
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _header_functions() == sorted(_abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _abi.lib()
+    for name in _header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_limits_match_binding():
+    text = open(HEADER).read()
+    for name in ("MOE_GROUP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_TOKENS", "MOE_MAX_D",
+                 "MOE_MAX_INTER", "MOE_BLOCK_ROWS", "MOE_TILE_ROWS", "MOE_LOGITS_IN"):
+        m = re.search(rf"#define {name} (\d+)", text)
+        assert m, name
+        if hasattr(_abi, name):
+            assert int(m.group(1)) == getattr(_abi, name), name
+
+
+def _layer(d=2048, inter=512, E=256, k=8, bias=False):
+    mats = [_abi.Q4Mat(FAKE, FAKE, FAKE) for _ in range(6)]
+    return _abi.Layer(d, inter, E, k, FAKE, FAKE if bias else None, *mats)
+
+
+def _routing():
+    return _abi.Routing(*[FAKE] * len(_abi.Routing._fields_))
+
+
+def _route(L, T=16, r=None, x=FAKE, flags=0):
+    lib = _abi.lib()
+    rr = r if r is not None else _routing()
+    return lib.moe_route(C.addressof(L), x, T, flags, C.addressof(rr), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=2000), _abi.MOE_EUNSUPPORTED),          # not a multiple of the group
+    (dict(inter=96), _abi.MOE_EUNSUPPORTED),
+    (dict(E=257), _abi.MOE_EUNSUPPORTED),
+    (dict(k=9, E=256), _abi.MOE_EUNSUPPORTED),
+    (dict(k=5, E=4), _abi.MOE_EUNSUPPORTED),        # k > E
+    (dict(d=0), _abi.MOE_EINVAL),
+    (dict(k=0), _abi.MOE_EINVAL),
+    (dict(d=8256), _abi.MOE_EUNSUPPORTED),
+    (dict(inter=2112), _abi.MOE_EUNSUPPORTED),
+])
+def test_route_rejects_unsupported_layers(kw, code):
+    assert _route(_layer(**kw)) == code
+    assert _abi.lib().moe_last_error()
+
+
+@pytest.mark.parametrize("T,code", [(0, _abi.MOE_EINVAL), (-3, _abi.MOE_EINVAL),
+                                    (_abi.MOE_MAX_TOKENS + 1, _abi.MOE_EUNSUPPORTED)])
+def test_route_rejects_bad_token_counts(T, code):
+    assert _route(_layer(), T=T) == code
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    lib = _abi.lib()
+    L = _layer()
+    r0 = _routing()
+    assert lib.moe_route(None, FAKE, 4, 0, C.addressof(r0), None) == _abi.MOE_EINVAL
+    assert _route(L, x=None) == _abi.MOE_EINVAL
+    assert _route(L, x=FAKE + 2) == _abi.MOE_EINVAL
+    L.gate.scale = None
+    assert _route(L) == _abi.MOE_EINVAL
+    assert b"gate.scale" in lib.moe_last_error()
+    L = _layer()
+    L.w_router = FAKE + 4
+    assert _route(L) == _abi.MOE_EINVAL
+    r = _routing()
+    r.perm = None
+    assert _route(_layer(), r=r) == _abi.MOE_EINVAL
+    assert b"perm" in lib.moe_last_error()
+    assert _route(_layer(), flags=0x10) == _abi.MOE_EINVAL
+
+
+def test_prefill_checks_workspace_size_before_launch():
+    lib = _abi.lib()
+    L = _layer()
+    need = lib.moe_workspace_bytes(C.addressof(L), 2048)
+    assert need > 0
+    r = _routing()
+    rc = lib.moe_prefill(C.addressof(L), FAKE, 2048, C.addressof(r), FAKE, need - 1, FAKE, None)
+    assert rc == _abi.MOE_EWORKSPACE
+    rc = lib.moe_decode(C.addressof(L), FAKE, 0, None, FAKE, lib.moe_workspace_bytes(
+        C.addressof(L), 1) - 256, FAKE, None)
+    assert rc == _abi.MOE_EWORKSPACE
+    rc = lib.moe_decode(C.addressof(L), FAKE, _abi.MOE_LOGITS_IN, None, FAKE, 1 << 30, FAKE, None)
+    assert rc == _abi.MOE_EINVAL
+
+
+def test_workspace_bytes_cover_the_staged_buffers():
+    lib = _abi.lib()
+    for T, d, I, E, k in ((2048, 2048, 512, 256, 8), (32, 512, 128, 32, 4), (1, 2048, 512, 256, 8)):
+        L = _layer(d, I, E, k)  # keep the struct alive across the call
+        n = lib.moe_workspace_bytes(C.addressof(L), T)
+        staged = 2 * (T * k * I + T * I + T * k * d)  # h, shared h, fp16 expert outputs
+        assert staged <= n <= staged + 2 * 4 * (d // 32) * E + 64 * 1024
+    bad = _layer(d=100)
+    assert lib.moe_workspace_bytes(C.addressof(bad), 16) == 0
+
+
+def test_block_map_capacity_bounds_the_tile_count():
+    lib = _abi.lib()
+    # sum over experts of ceil(c/rows) <= floor(T*k/rows) + min(E, T*k)
+    assert lib.moe_block_map_capacity(2048, 8, 256, 32) == 512 + 256
+    assert lib.moe_block_map_capacity(2048, 8, 256, 128) == 128 + 256
+    assert lib.moe_block_map_capacity(1, 8, 256, 32) == 0 + 8
+    assert lib.moe_block_map_capacity(0, 8, 256, 32) == 0
+
+
+def test_dequant_rejects_bad_shapes():
+    lib = _abi.lib()
+    m = _abi.Q4Mat(FAKE, FAKE, FAKE)
+    assert lib.moe_dequant(C.addressof(m), 4, 100, FAKE, None) == _abi.MOE_EUNSUPPORTED
+    assert lib.moe_dequant(C.addressof(m), 0, 64, FAKE, None) == _abi.MOE_EINVAL
+    assert lib.moe_dequant(None, 4, 64, FAKE, None) == _abi.MOE_EINVAL
+
+
+def test_strerror_names_every_code():
+    lib = _abi.lib()
+    names = {lib.moe_strerror(c) for c in (0, -1, -2, -3, -4)}
+    assert len(names) == 5

@@ -1,0 +1,265 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars:
+  - dequantisation, routing indices, counts, offsets, perm, inv_perm and both
+    block maps: bit-exact, routing done from the oracle's fp32 logits;
+  - router logits: max |err| <= 1e-3 * RMS(oracle logits);
+  - renormalised scores: |err| <= 2e-6 (fp32 against the oracle's fp64);
+  - layer outputs (bf16): max |y - y_exact| <= 2e-2 * RMS(y_exact), y_exact the
+    oracle's unrounded fp64 sum; run-to-run bit-identical.
+Full-size workloads are checked on sampled tokens (the oracle computes each
+output token independently); small shapes on every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q4_routed_expert_amd as q4
+from workloads import (WORKLOADS, bits_to_f32, decode_inputs, make_layer, random_layer,
+                       random_x)
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 2e-2
+LOGIT_TOL = 1e-3
+W_TOL = 2e-6
+
+
+def log(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def xdev(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def y_error(y_bits, y_exact):
+    err = np.abs(bits_to_f32(y_bits).astype(np.float64) - y_exact)
+    rms = float(np.sqrt(np.mean(y_exact ** 2)))
+    return float(err.max()) / rms, rms
+
+
+def compare_routing(r, ref, T, E, k, bm_ref, tm_ref):
+    torch.cuda.synchronize()
+    assert np.array_equal(r.topk_idx.cpu().numpy(), ref["idx"])
+    assert np.abs(r.topk_w.cpu().numpy() - ref["w"]).max() <= W_TOL
+    assert np.array_equal(r.counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(r.offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(r.perm.cpu().numpy(), ref["perm"])
+    assert np.array_equal(r.inv_perm.cpu().numpy(), ref["inv_perm"])
+    nb, nt = int(r.n_blocks.item()), int(r.n_tiles.item())
+    assert nb == bm_ref[1] and nt == tm_ref[1]
+    assert np.array_equal(r.block_map.cpu().numpy()[:nb], bm_ref[0])
+    assert np.array_equal(r.tile_map.cpu().numpy()[:nt], tm_ref[0])
+
+
+def oracle_routing(logits, k):
+    ref = oracle.route(logits, k)
+    bm = oracle.block_map(ref["counts"], ref["offsets"], q4.BLOCK_ROWS)
+    tm = oracle.block_map(ref["counts"], ref["offsets"], q4.TILE_ROWS)
+    return ref, bm, tm
+
+
+def sample_tokens(T, seed, n=12):
+    rng = np.random.default_rng(seed)
+    pick = {0, 1, T // 2, T - 2, T - 1} | set(rng.integers(0, T, n).tolist())
+    return np.array(sorted(t for t in pick if 0 <= t < T), np.int32)
+
+
+def run_layer_case(L, x, dev, tokens=None, name=""):
+    """Route on the GPU from the oracle's logits, run prefill, compare."""
+    T, E, k = x.shape[0], L["n_experts"], L["top_k"]
+    layer = q4.DeviceLayer.from_host(L, dev)
+    xd = xdev(x, dev)
+    l_ref = oracle.router_logits(x, L["w_router"], L.get("router_bias"))
+    # router logits computed on the GPU
+    r_own = q4.route(layer, xd)
+    torch.cuda.synchronize()
+    l_gpu = r_own.logits.cpu().numpy()
+    lrms = float(np.sqrt(np.mean(l_ref.astype(np.float64) ** 2)))
+    lerr = float(np.abs(l_gpu.astype(np.float64) - l_ref).max()) / lrms
+    own_idx = r_own.topk_idx.cpu().numpy()
+    # routing from identical logits: bit-exact
+    ref, bm, tm = oracle_routing(l_ref, k)
+    r = q4.DeviceRouting(T, E, k, dev)
+    r.logits.copy_(torch.from_numpy(l_ref))
+    q4.route(layer, xd, routing=r, logits_in=True)
+    compare_routing(r, ref, T, E, k, bm, tm)
+    differ = int((np.sort(own_idx, 1) != np.sort(ref["idx"], 1)).any(1).sum())
+    ws = q4.workspace(layer, T, dev)
+    y = q4.prefill(layer, xd, r, ws)
+    y2 = q4.prefill(layer, xd, r, ws)
+    torch.cuda.synchronize()
+    yb, yb2 = host_bits(y), host_bits(y2)
+    assert np.array_equal(yb, yb2), "prefill is not run-to-run deterministic"
+    if tokens is None:
+        tokens = np.arange(T, dtype=np.int32)
+    y_exact, _ = oracle.layer_tokens(L, x, tokens, ref["idx"], ref["w"])
+    err, rms = y_error(yb[tokens], y_exact)
+    log(f"{name} T={T} E={E} k={k}: logits err/rms={lerr:.2e}, tokens whose expert set "
+        f"differs on GPU logits={differ}, y max err/rms={err:.3e} (rms {rms:.3f}, "
+        f"{len(tokens)} tokens)")
+    assert lerr <= LOGIT_TOL
+    assert err <= Y_TOL
+    return err
+
+
+# ------------------------------------------------------------------ dequantisation
+
+def test_dequant_bit_exact(dev):
+    rng = np.random.default_rng(7)
+    Lr = random_layer(rng, d=512, inter=96 * 2, E=2, k=1)
+    for name in ("gate", "down"):
+        q, s, b = Lr[name + "_q"][1], Lr[name + "_s"][1], Lr[name + "_b"][1]
+        ref = oracle.dequant(q, s, b)
+        got = q4.dequant(q4._dev(q, dev), q4._dev(s, dev), q4._dev(b, dev))
+        assert np.array_equal(host_bits(got), ref)
+    # exact round-to-nearest-even ties: w = 1 + q/256 with bf16 spacing 2^-7
+    q = np.array([[0x76543210, 0xFEDCBA98] * 4], np.uint32)
+    s = np.array([[0x3B80]], np.uint16)
+    b = np.array([[0x3F80]], np.uint16)
+    got = q4.dequant(q4._dev(q, dev), q4._dev(s, dev), q4._dev(b, dev))
+    assert np.array_equal(host_bits(got), oracle.dequant(q, s, b))
+
+
+# ------------------------------------------------------------------ workloads
+
+@pytest.mark.parametrize("name", ["tiny", "prefill512", "prefill2048", "skew4096"])
+def test_workload_layer(name, dev):
+    w = WORKLOADS[name]
+    L, x = make_layer(w)
+    tokens = None if w.T <= 64 else sample_tokens(w.T, w.seed)
+    if name == "skew4096":  # include tokens of the hottest and of the rarest experts
+        l_ref = oracle.router_logits(x, L["w_router"], L["router_bias"])
+        ref = oracle.route(l_ref, w.top_k)
+        c = ref["counts"]
+        rare = np.where((c > 0) & (c <= 4))[0]
+        extra = [ref["perm"][ref["offsets"][e]] // w.top_k for e in rare[:4]]
+        tokens = np.array(sorted(set(tokens.tolist()) | set(int(t) for t in extra)), np.int32)
+    run_layer_case(L, x, dev, tokens, name)
+
+
+def test_decode_workload(dev):
+    w = WORKLOADS["decode"]
+    xs = decode_inputs(w, 6)
+    for layer_i, steps in ((0, (0, 1, 2)), (7, (3, 4, 5))):
+        L, _ = make_layer(w, layer_i)
+        layer = q4.DeviceLayer.from_host(L, dev)
+        ws = q4.workspace(layer, 1, dev)
+        for st in steps:
+            x = xs[st:st + 1]
+            xd = xdev(x, dev)
+            ref_all = oracle.layer(L, x)
+            r = q4.DeviceRouting(1, w.n_experts, w.top_k, dev)
+            y_own = q4.decode(layer, xd, ws, routing=r)
+            torch.cuda.synchronize()
+            l_gpu = r.logits.cpu().numpy()
+            lrms = float(np.sqrt(np.mean(ref_all["logits"].astype(np.float64) ** 2)))
+            lerr = float(np.abs(l_gpu - ref_all["logits"]).max()) / lrms
+            # from identical logits: same experts, same scores, y within tolerance
+            r.logits.copy_(torch.from_numpy(ref_all["logits"]))
+            y = q4.decode(layer, xd, ws, routing=r, logits_in=True)
+            y_again = q4.decode(layer, xd, ws, routing=r, logits_in=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(r.topk_idx.cpu().numpy(), ref_all["idx"])
+            assert np.abs(r.topk_w.cpu().numpy() - ref_all["w"]).max() <= W_TOL
+            err, rms = y_error(host_bits(y), ref_all["y_exact"])
+            err_own, _ = y_error(host_bits(y_own), ref_all["y_exact"])
+            assert np.array_equal(host_bits(y), host_bits(y_again))
+            log(f"decode layer {layer_i} step {st}: logits err/rms={lerr:.2e}, y err/rms="
+                f"{err:.3e} (own routing {err_own:.3e}), rms {rms:.3f}")
+            assert lerr <= LOGIT_TOL
+            assert err <= Y_TOL
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = [
+    # (T, d, inter, E, k, router_bias, seed)
+    (1, 256, 128, 8, 2, False, 1),        # single token
+    (33, 576, 192, 40, 3, False, 2),      # K not a multiple of 128, E not of 64, odd k
+    (600, 256, 128, 4, 2, False, 3),      # several 128-row tiles per expert, ragged tails
+    (70, 256, 128, 8, 8, False, 4),       # k = E: every expert selected
+    (100, 256, 128, 256, 8, False, 5),    # most experts empty
+    (129, 256, 64, 16, 1, True, 6),       # k = 1, one row past a tile
+]
+
+
+@pytest.mark.parametrize("T,d,inter,E,k,bias,seed", EDGE)
+def test_edge_shapes(T, d, inter, E, k, bias, seed, dev):
+    rng = np.random.default_rng(1000 + seed)
+    L = random_layer(rng, d, inter, E, k, router_bias=bias)
+    x = random_x(rng, T, d)
+    run_layer_case(L, x, dev, None, f"edge{seed}")
+
+
+def test_all_tokens_pick_the_same_experts(dev):
+    # a dominant router bias sends every token to experts 5, 2, 9, 0: four
+    # experts with T rows each (several tiles), every other expert empty
+    rng = np.random.default_rng(77)
+    T, E, k = 300, 32, 4
+    L = random_layer(rng, 256, 128, E, k, router_bias=True)
+    L["router_bias"] = np.zeros(E, np.float32)
+    L["router_bias"][[5, 2, 9, 0]] = [40.0, 30.0, 20.0, 10.0]
+    x = random_x(rng, T, 256)
+    run_layer_case(L, x, dev, None, "one-hot")
+
+
+def test_routing_ties_and_signed_zeros(dev):
+    # coarse logits with many exact ties (and -0.0 vs +0.0) given to the GPU
+    rng = np.random.default_rng(8)
+    T, E, k = 257, 64, 8
+    L = random_layer(rng, 128, 64, E, k)
+    l = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    l[l == 0] = np.where(rng.random(int((l == 0).sum())) < 0.5, -0.0, 0.0)
+    layer = q4.DeviceLayer.from_host(L, dev)
+    ref, bm, tm = oracle_routing(l, k)
+    r = q4.DeviceRouting(T, E, k, dev)
+    r.logits.copy_(torch.from_numpy(l))
+    q4.route(layer, xdev(random_x(rng, T, 128), dev), routing=r, logits_in=True)
+    compare_routing(r, ref, T, E, k, bm, tm)
+
+
+def test_routing_at_the_token_limit(dev):
+    rng = np.random.default_rng(9)
+    T, E, k = 32768, 256, 8
+    L = random_layer(rng, 64, 64, E, k)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l[:, 17] += 2.5  # one hot expert with ~T rows
+    layer = q4.DeviceLayer.from_host(L, dev)
+    ref, bm, tm = oracle_routing(l, k)
+    r = q4.DeviceRouting(T, E, k, dev)
+    r.logits.copy_(torch.from_numpy(l))
+    q4.route(layer, xdev(np.zeros((T, 64), np.uint16), dev), routing=r, logits_in=True)
+    compare_routing(r, ref, T, E, k, bm, tm)
+    log(f"routing T={T}: n_blocks={bm[1]} n_tiles={tm[1]} max count={ref['counts'].max()}")
+
+
+def test_small_decode_shapes(dev):
+    rng = np.random.default_rng(10)
+    for d, inter, E, k, bias in ((576, 192, 40, 3, True), (256, 128, 8, 8, False)):
+        L = random_layer(rng, d, inter, E, k, router_bias=bias)
+        layer = q4.DeviceLayer.from_host(L, dev)
+        ws = q4.workspace(layer, 1, dev)
+        x = random_x(rng, 1, d)
+        ref = oracle.layer(L, x)
+        r = q4.DeviceRouting(1, E, k, dev)
+        r.logits.copy_(torch.from_numpy(ref["logits"]))
+        y = q4.decode(layer, xdev(x, dev), ws, routing=r, logits_in=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(r.topk_idx.cpu().numpy(), ref["idx"])
+        err, _ = y_error(host_bits(y), ref["y_exact"])
+        log(f"decode d={d} I={inter} E={E} k={k}: y err/rms={err:.3e}")
+        assert err <= Y_TOL
