@@ -161,7 +161,7 @@ def bench_prefill(args, q4, torch, ev, stream):
     work = prefill_work(w.T, w.d, w.inter, w.n_experts, w.top_k, counts)
     sec = ms_step / 1e3
     tflops = work["flops"] / sec / 1e12
-    log(f"prefill: {ms_step * 1e3:.1f} us/layer ({wall / K * 1e3:.1f} us wall), "
+    log(f"prefill: {ms_step * 1e3:.1f} us/layer ({wall / K * 1e6:.1f} us wall), "
         f"{tflops:.1f} TFLOP/s, per kernel (us): " +
         ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per.items()))
     out = {
@@ -197,13 +197,13 @@ def bench_decode(args, q4, torch, ev, stream):
         q4.decode(layers[li], xs[0:1], ws, y)
     torch.cuda.synchronize()
     mid = n_steps // 2
-    ev_d = [ev.make(4) for _ in range(n_layers)]
+    ev_d = [ev.make(5) for _ in range(n_layers)]
     t = ev.make(2)
     ev.record(t[0], stream)
     for st in range(n_steps):
         for li in range(n_layers):
             if st == mid:
-                lib.moe_trace_events(C.cast(ev_d[li], C.c_void_p), 4)
+                lib.moe_trace_events(C.cast(ev_d[li], C.c_void_p), 5)
             q4.decode(layers[li], xs[st:st + 1], ws, y)
             if st == mid:
                 lib.moe_trace_events(None, 0)
@@ -211,7 +211,7 @@ def bench_decode(args, q4, torch, ev, stream):
     torch.cuda.synchronize()
     calls = n_steps * n_layers
     us_layer = ev.ms(t[0], t[1]) * 1e3 / calls
-    names = ["router", "gate_up", "down"]
+    names = ["router_partial", "router_topk", "gate_up", "down"]
     per = {n: sum(ev.ms(ev_d[li][j], ev_d[li][j + 1]) for li in range(n_layers)) * 1e3 / n_layers
            for j, n in enumerate(names)}
     expert_bytes = (w.top_k + 1) * (2 * q4_bytes(w.inter, w.d) + q4_bytes(w.d, w.inter))
@@ -255,7 +255,7 @@ def bench_decode(args, q4, torch, ev, stream):
     out["roofline"] = {"bound": "hbm", "achieved": round(ex_bytes / k_sec / 1e9, 1),
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                        "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
-                       "kernels": "decode_router + decode_gate_up + decode_down"}
+                       "kernels": "decode router partial + router top-k + gate/up + down"}
     del layers, ws
     torch.cuda.empty_cache()
     return out
@@ -285,7 +285,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-layers", type=int, default=40)
-    ap.add_argument("--cpu-tokens", type=int, default=48)
+    ap.add_argument("--cpu-tokens", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")

@@ -137,8 +137,7 @@ int32_t moe_block_map_capacity(int32_t T, int32_t top_k, int32_t n_experts, int3
    need for this layer shape: the gate/up activations h (bf16), the shared
    expert's activations, the routed experts' fp16 outputs before the combine,
    and the decode path's router partial sums.  0 on invalid arguments.  The
-   workspace must be zero-filled once before its first use by moe_decode
-   (moe_decode leaves its counter at zero again on exit). */
+   contents need no initialisation and are not preserved between calls. */
 size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
 
 /* Routing of T tokens, entirely on the device, no host synchronisation:
@@ -176,8 +175,10 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
 /* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill and
    moe_decode call made on this host thread records events[0] on its stream
    before its first kernel and events[i] right after its i-th kernel, for
-   i < n (moe_route: 3 kernels, 2 with MOE_LOGITS_IN; moe_prefill: gate/up,
-   down, shared down + combine; moe_decode: router, gate/up, down).  The
+   i < n (moe_route: router logits, top-k, sort; moe_prefill: gate/up, down,
+   shared down + combine; moe_decode: router partial sums, router sum +
+   top-k, gate/up, down).  With MOE_LOGITS_IN the router-logit slot is still
+   recorded but brackets no kernel.  The
    elapsed time between consecutive events is one kernel's duration.  events
    are hipEvent_t handles created and owned by the caller; pass NULL to stop. */
 void moe_trace_events(void* const* events, int32_t n);

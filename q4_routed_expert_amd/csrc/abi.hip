@@ -95,16 +95,14 @@ int check_routing(const moe_routing* r) {
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace: [decode region | prefill region].  The decode region comes first
-// and prefill never writes it, so the decode arrival counter stays zero
-// between calls even when one workspace serves both.
+// Workspace: [decode region | prefill region], so one workspace sized for T
+// tokens serves both entry points.
 struct DecodeWs {
-    size_t counter, sel_idx, sel_w, logits, partial, h, total;
+    size_t sel_idx, sel_w, logits, partial, h, total;
 };
 DecodeWs decode_ws(const moe_layer* L) {
     DecodeWs w;
     size_t o = 0;
-    w.counter = o; o += 256;
     w.sel_idx = o; o += align256(sizeof(int32_t) * MOE_MAX_TOPK);
     w.sel_w = o; o += align256(sizeof(float) * MOE_MAX_TOPK);
     w.logits = o; o += align256(sizeof(float) * L->n_experts);
@@ -171,10 +169,12 @@ int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
     if (!logits_in && (rc = check_ptr(x, "x"))) return rc;
     hipStream_t s = (hipStream_t)stream;
     trace_begin(s);
-    if (!logits_in &&
-        (rc = hip_status(q4moe::launch_router_logits(x, T, L->d, L->w_router, L->router_bias,
-                                                     L->n_experts, r->logits, s),
-                         "router logits")))
+    if (logits_in)
+        q4moe::trace_point(s);
+    else if ((rc = hip_status(q4moe::launch_router_logits(x, T, L->d, L->w_router,
+                                                          L->router_bias, L->n_experts,
+                                                          r->logits, s),
+                              "router logits")))
         return rc;
     if ((rc = hip_status(q4moe::launch_topk(r->logits, T, L->n_experts, L->top_k, r->topk_idx,
                                             r->topk_w, s),
@@ -262,7 +262,6 @@ int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_
     a.out_idx = r ? r->topk_idx : nullptr;
     a.out_w = r ? r->topk_w : nullptr;
     a.partial = (float*)(base + dw.partial);
-    a.counter = (uint32_t*)(base + dw.counter);
     a.sel_idx = (int32_t*)(base + dw.sel_idx);
     a.sel_w = (float*)(base + dw.sel_w);
     a.h = (uint16_t*)(base + dw.h);

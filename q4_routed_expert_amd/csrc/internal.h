@@ -52,7 +52,6 @@ struct DecodeArgs {
     int32_t* out_idx;    // [k] or NULL
     float* out_w;        // [k] or NULL
     float* partial;      // [d/32][E] router partial sums
-    uint32_t* counter;   // arrival counter, zero between calls
     int32_t* sel_idx;    // [k]
     float* sel_w;        // [k]
     uint16_t* h;         // bf16 [k+1][I]

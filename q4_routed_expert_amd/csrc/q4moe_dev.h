@@ -62,19 +62,27 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
 // so is the sum whenever the exponents of s and b lie within 12 of each other,
 // so the single fp32 fma followed by the round-to-nearest-even conversion
 // gives the nearest bf16 to the exact affine value.
+//
+// 23 VALU instructions per word: 3 to split the even and odd codes into the
+// four bytes of two words, 8 v_cvt_f32_ubyte{0..3} (each converts one byte in
+// place), 8 v_fma_f32 and 4 v_cvt_pk_bf16_f32.  The empty asm statements hide
+// the masks from known-bits analysis, which would otherwise turn each byte
+// read into a 4-bit extract plus a separate convert.
 __device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float b) {
-    const uint32_t ev = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-    bf16x8 r;
-    r[0] = (__bf16)__builtin_fmaf((float)(ev & 0xFFu), s, b);
-    r[1] = (__bf16)__builtin_fmaf((float)(od & 0xFFu), s, b);
-    r[2] = (__bf16)__builtin_fmaf((float)((ev >> 8) & 0xFFu), s, b);
-    r[3] = (__bf16)__builtin_fmaf((float)((od >> 8) & 0xFFu), s, b);
-    r[4] = (__bf16)__builtin_fmaf((float)((ev >> 16) & 0xFFu), s, b);
-    r[5] = (__bf16)__builtin_fmaf((float)((od >> 16) & 0xFFu), s, b);
-    r[6] = (__bf16)__builtin_fmaf((float)(ev >> 24), s, b);
-    r[7] = (__bf16)__builtin_fmaf((float)(od >> 24), s, b);
-    return r;
+    uint32_t ev = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
+    uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+    asm("" : "+v"(ev));
+    asm("" : "+v"(od));
+    u32x4 r;
+    r[0] = pack_bf16x2(__builtin_fmaf((float)(ev & 0xFFu), s, b),
+                       __builtin_fmaf((float)(od & 0xFFu), s, b));
+    r[1] = pack_bf16x2(__builtin_fmaf((float)((ev >> 8) & 0xFFu), s, b),
+                       __builtin_fmaf((float)((od >> 8) & 0xFFu), s, b));
+    r[2] = pack_bf16x2(__builtin_fmaf((float)((ev >> 16) & 0xFFu), s, b),
+                       __builtin_fmaf((float)((od >> 16) & 0xFFu), s, b));
+    r[3] = pack_bf16x2(__builtin_fmaf((float)(ev >> 24), s, b),
+                       __builtin_fmaf((float)(od >> 24), s, b));
+    return __builtin_bit_cast(bf16x8, r);
 }
 
 // acc + sum over the eight weights of one code word of bf16(q*s + b) * v, with

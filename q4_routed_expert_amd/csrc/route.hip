@@ -12,61 +12,92 @@ namespace q4moe {
 
 // ---------------------------------------------------------------------------
 // Router logits l[t][e] = sum_j x[t][j] * W_r[j][e] (+ b[e]).
-// x is bf16, W_r fp32.  W_r is split on chip into bf16 hi + lo parts
-// (hi = bf16(w), lo = bf16(w - hi), residual below 2^-16 |w|) so the
-// contraction runs on bf16 MFMA with fp32 accumulation.  Work group: 64
-// tokens x 64 experts, four waves of 32x32, K step 32.
+// x is bf16, W_r fp32.  Each W_r value is split on chip into bf16 hi + lo
+// parts (hi = bf16(w), lo = bf16(w - hi); the residual is below 2^-16 |w|) so
+// the contraction runs on bf16 MFMA with fp32 accumulation: x*hi + x*lo.
+// Work group: 64 tokens x 32 experts, four waves splitting K into quarters;
+// each wave loads its operands straight from memory (x: 16 bytes per lane
+// per M-fragment; W_r: one fp32 per lane per k, 32 consecutive experts per
+// row = one 128-byte line) one K-step ahead of the matrix cores, and the four
+// partial tiles are added in a fixed order through LDS at the end.
 // ---------------------------------------------------------------------------
-constexpr int kRtM = 64, kRtN = 64, kRtK = 32, kRtPad = 8;
+constexpr int kRtM = 64, kRtN = 32;
+
+__device__ __forceinline__ void split_hi_lo(const float (&w)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hi[i] = (__bf16)w[i];
+        lo[i] = (__bf16)(w[i] - (float)hi[i]);
+    }
+}
 
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ x, int T, int d, const float* __restrict__ W,
     const float* __restrict__ bias, int E, float* __restrict__ logits) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kRtM][kRtK + kRtPad];
-    __shared__ __attribute__((aligned(16))) uint16_t wh[kRtN][kRtK + kRtPad];
-    __shared__ __attribute__((aligned(16))) uint16_t wl[kRtN][kRtK + kRtPad];
+    constexpr int S = 4;  // K-steps in flight per wave
+    __shared__ float red[3][2][16][64];
     const int t0 = blockIdx.x * kRtM, e0 = blockIdx.y * kRtN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc = {};
-    for (int k0 = 0; k0 < d; k0 += kRtK) {
-        {  // x tile: 64 rows x 32 bf16, one 16-byte piece per thread
-            const int row = tid >> 2, c = tid & 3, t = t0 + row;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (t < T) v = *(const u32x4*)(x + (size_t)t * d + k0 + 8 * c);
-            *(u32x4*)&xs[row][8 * c] = v;
-        }
-        {  // W tile: 32 k x 64 experts fp32, stored transposed as bf16 hi / lo
-            const int kk = tid >> 3, c8 = (tid & 7) * 8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int n = e0 + (lane & 31);
+    const bool n_ok = n < E;
+    const int kq = d / 4;  // K range of this wave (d % 64 == 0)
+    const int kbeg = wave * kq, kend = kbeg + kq;
+    const int n_steps = (kq / 16 + S - 1) / S * S;  // padded; steps past kend add zeros
+    const int ta = t0 + (lane & 31), tb = ta + 32;
+    // clamped, always-valid addresses: loads stay outside branches (see the
+    // grouped GEMM) and invalid values are zeroed where they are used
+    const uint16_t* xa = x + (size_t)(ta < T ? ta : 0) * d;
+    const uint16_t* xb = x + (size_t)(tb < T ? tb : 0) * d;
+    const float* wcol = W + (n_ok ? n : 0);
+    f32x16 acc0 = {}, acc1 = {};
+    float wv[S][8];
+    u32x4 av[S], bv[S];
+    auto load = [&](int st, int k) {
+        const int kk = (k < kend ? k : kbeg) + 8 * half;
+        av[st] = *(const u32x4*)(xa + kk);
+        bv[st] = *(const u32x4*)(xb + kk);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = e0 + c8 + i;
-                const float f = e < E ? W[(size_t)(k0 + kk) * E + e] : 0.0f;
-                const uint16_t hi = f32_to_bf16(f);
-                wh[c8 + i][kk] = hi;
-                wl[c8 + i][kk] = f32_to_bf16(f - bf16_to_f32(hi));
-            }
-        }
-        __syncthreads();
+        for (int i = 0; i < 8; ++i) wv[st][i] = wcol[(size_t)(kk + i) * E];
+    };
 #pragma unroll
-        for (int j = 0; j < kRtK / 16; ++j) {
-            const int kk = 16 * j + 8 * (lane >> 5);
-            const bf16x8 a = *(const bf16x8*)&xs[32 * wm + (lane & 31)][kk];
-            const bf16x8 bh = *(const bf16x8*)&wh[32 * wn + (lane & 31)][kk];
-            const bf16x8 bl = *(const bf16x8*)&wl[32 * wn + (lane & 31)][kk];
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
+    for (int u = 0; u < S - 1; ++u) load(u, kbeg + 16 * u);
+    for (int s0 = 0; s0 < n_steps; s0 += S) {
+#pragma unroll
+        for (int u = 0; u < S; ++u) {
+            const int k = kbeg + 16 * (s0 + u);
+            const bool ok = k < kend && n_ok;
+            float w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = ok ? wv[u][i] : 0.0f;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const bf16x8 A0 = __builtin_bit_cast(bf16x8, ta < T ? av[u] : z);
+            const bf16x8 A1 = __builtin_bit_cast(bf16x8, tb < T ? bv[u] : z);
+            bf16x8 hi, lo;
+            split_hi_lo(w, hi, lo);
+            load((u + S - 1) % S, k + 16 * (S - 1));
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, hi, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, hi, acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, lo, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, lo, acc1, 0, 0, 0);
         }
-        __syncthreads();
     }
-    const int n = e0 + 32 * wn + (lane & 31);
-    if (n < E) {
-        const float bb = bias ? bias[n] : 0.0f;
+    if (wave > 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int t = t0 + 32 * wm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (t < T) logits[(size_t)t * E + n] = acc[i] + bb;
+            red[wave - 1][0][i][lane] = acc0[i];
+            red[wave - 1][1][i][lane] = acc1[i];
         }
+    }
+    __syncthreads();
+    if (wave > 0 || !n_ok) return;
+    const float bb = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+        const float v0 = ((acc0[i] + red[0][0][i][lane]) + red[1][0][i][lane]) + red[2][0][i][lane];
+        const float v1 = ((acc1[i] + red[0][1][i][lane]) + red[1][1][i][lane]) + red[2][1][i][lane];
+        if (t0 + r < T) logits[(size_t)(t0 + r) * E + n] = v0 + bb;
+        if (t0 + 32 + r < T) logits[(size_t)(t0 + 32 + r) * E + n] = v1 + bb;
     }
 }
 
