@@ -90,10 +90,10 @@ def prefill_work(T, d, I, E, k, counts):
         "flops": f_gu + f_dn_routed + f_dn_shared,
         "bytes": gu_w + dn_w + 4 * d * E + x_b + y_b,
         "gate_up": {"flops": f_gu, "bytes": gu_w + x_b + h_b + hs_b},
-        "down": {"flops": f_dn_routed,
-                 "bytes": touched * q4_bytes(d, I) + h_b + 2 * T * k * d},
-        "shared_down_combine": {"flops": f_dn_shared,
-                                "bytes": q4_bytes(d, I) + hs_b + 2 * T * k * d + y_b},
+        "down": {"flops": f_dn_routed + f_dn_shared,
+                 "bytes": dn_w + h_b + hs_b + 2 * T * k * d + 4 * T * d},
+        "combine": {"flops": 2 * T * k * d + T * d,
+                    "bytes": 2 * T * k * d + 4 * T * d + 4 * T * k + y_b},
     }
 
 
@@ -150,7 +150,7 @@ def bench_prefill(args, q4, torch, ev, stream):
     wall = time.perf_counter() - wall0
     ms_step = ev.ms(t[0], t[1]) / K
     names_r = ["router_logits", "topk", "route_sort"]
-    names_p = ["gate_up", "down", "shared_down_combine"]
+    names_p = ["gate_up", "down", "combine"]
     per = {n: 0.0 for n in names_r + names_p}
     for i in range(K):
         for j, n in enumerate(names_r):
@@ -171,7 +171,7 @@ def bench_prefill(args, q4, torch, ev, stream):
     }
     gu_sec = per["gate_up"] / 1e3
     out["roofline"] = roofline(work["gate_up"]["flops"], work["gate_up"]["bytes"], gu_sec)
-    out["roofline"]["kernel"] = "expert_gemm_kernel<4,0> (gate/up grouped GEMM + SiLU*up)"
+    out["roofline"]["kernel"] = "gate_up_kernel (grouped gate/up GEMM + SiLU*up)"
     out["roofline"]["mfma_frac"] = round(work["gate_up"]["flops"] / gu_sec / 1e12 / PEAK_BF16_TFLOPS, 4)
     del layers, ws
     torch.cuda.empty_cache()

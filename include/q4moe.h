@@ -135,8 +135,9 @@ int32_t moe_block_map_capacity(int32_t T, int32_t top_k, int32_t n_experts, int3
 
 /* Bytes of device workspace moe_prefill (T tokens) and moe_decode (T = 1)
    need for this layer shape: the gate/up activations h (bf16), the shared
-   expert's activations, the routed experts' fp16 outputs before the combine,
-   and the decode path's router partial sums.  0 on invalid arguments.  The
+   expert's activations, the routed experts' fp16 outputs and the shared
+   expert's fp32 outputs before the combine, and the decode path's router
+   partial sums.  0 on invalid arguments.  The
    contents need no initialisation and are not preserved between calls. */
 size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
 
@@ -150,9 +151,9 @@ int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
 
 /* The expert part of the layer for T tokens routed by moe_route: grouped
    gate/up GEMM with fused SiLU(gate)*up over the expert-sorted rows plus the
-   shared expert over all tokens, then the down projection of the routed rows,
-   then the shared expert's down projection fused with the fixed-order combine
-   (slots in order, scores applied, shared expert last).  Dequantisation
+   shared expert over all tokens, then the down projections of the routed rows
+   and of the shared expert, then the fixed-order combine (slots in order,
+   scores applied, shared expert last).  Dequantisation
    happens on chip, tile by tile; accumulation is fp32; y: bf16 [T][d].
    ws must hold moe_workspace_bytes(L, T) bytes. */
 int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r,
@@ -175,8 +176,8 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
 /* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill and
    moe_decode call made on this host thread records events[0] on its stream
    before its first kernel and events[i] right after its i-th kernel, for
-   i < n (moe_route: router logits, top-k, sort; moe_prefill: gate/up, down,
-   shared down + combine; moe_decode: router partial sums, router sum +
+   i < n (moe_route: router logits, top-k, sort; moe_prefill: gate/up, down
+   (routed and shared), combine; moe_decode: router partial sums, router sum +
    top-k, gate/up, down).  With MOE_LOGITS_IN the router-logit slot is still
    recorded but brackets no kernel.  The
    elapsed time between consecutive events is one kernel's duration.  events

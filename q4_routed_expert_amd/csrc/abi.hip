@@ -112,7 +112,7 @@ DecodeWs decode_ws(const moe_layer* L) {
     return w;
 }
 struct PrefillWs {
-    size_t h, h_sh, part, total;
+    size_t h, h_sh, part, sh_out, total;
 };
 PrefillWs prefill_ws(const moe_layer* L, int32_t T, size_t base) {
     PrefillWs w;
@@ -121,6 +121,7 @@ PrefillWs prefill_ws(const moe_layer* L, int32_t T, size_t base) {
     w.h = o; o += align256(sizeof(uint16_t) * A * L->inter);
     w.h_sh = o; o += align256(sizeof(uint16_t) * (size_t)T * L->inter);
     w.part = o; o += align256(sizeof(uint16_t) * A * L->d);
+    w.sh_out = o; o += align256(sizeof(float) * (size_t)T * L->d);
     w.total = o;
     return w;
 }
@@ -217,6 +218,7 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
     a.h = (uint16_t*)(base + pw.h);
     a.h_sh = (uint16_t*)(base + pw.h_sh);
     a.part = (uint16_t*)(base + pw.part);
+    a.sh_out = (float*)(base + pw.sh_out);
     a.y = y;
     trace_begin((hipStream_t)stream);
     return hip_status(q4moe::launch_prefill(a, (hipStream_t)stream), "prefill");

@@ -35,7 +35,8 @@ struct PrefillArgs {
     int tile_bound;      // host upper bound on *n_tiles
     uint16_t* h;         // bf16 [T*k][I], expert-sorted rows
     uint16_t* h_sh;      // bf16 [T][I]
-    uint16_t* part;      // fp16 [T*k][d], rows in assignment order
+    uint16_t* part;      // fp16 [T*k][d], routed expert outputs, rows in assignment order
+    float* sh_out;       // fp32 [T][d], the shared expert's outputs
     uint16_t* y;         // bf16 [T][d]
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);

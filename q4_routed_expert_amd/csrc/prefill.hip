@@ -1,46 +1,41 @@
 // prefill.hip -- the expert part of one MoE layer for a chunk of T tokens:
 //   (1) grouped gate/up GEMM over the expert-sorted rows, SiLU(gate)*up fused,
 //       plus the shared expert over all tokens            -> h, h_sh (bf16)
-//   (2) grouped down GEMM of the routed rows               -> part (fp16)
-//   (3) shared expert's down GEMM fused with the combine:
-//       y_t = bf16( sum_s w[t,s] * part[t*k+s] (slot order) + shared )
+//   (2) grouped down GEMM of the routed rows -> part (fp16, one row per
+//       assignment) and of the shared expert -> sh_out (fp32, one row per token)
+//   (3) the fixed-order combine:
+//       y_t = bf16( sum_s w[t,s] * part[t*k+s] (slot order) + sh_out[t] )
 // Sources: [Lily-M5] = "Perplexity's Lily beats MLX-LM on MacBook M5 because
 // it only runs one model".  Section "Prefill: keep routing on the GPU,
 // dequantize in flight": the grouped GEMM dequantises one small Q4 tile at a
 // time on chip, accumulates in FP32, writes bf16, never materialises the
 // expanded weights; 32-row tiles.  Section "Decode: minimize bytes per token":
-// expert input projections fused with the gate activation, the output
-// projection with the routing scores and the shared expert.
+// the output projection is combined with the routing scores and the shared
+// expert.
 //
-// Kernel design (gfx950).  One work item = up to 128 expert-sorted rows of
-// one expert (the 128-row work map written by the routing) x one block of
-// output columns.  A work group has 8 waves (two per SIMD); each wave owns 32
-// output columns of one weight matrix (for gate/up: waves 0-3 gate, 4-7 up,
-// on the same 128 intermediate columns; for the down GEMMs: 256 columns).
-// Per K chunk of 128 (two quantisation groups):
-//   - the activation rows (gathered through perm for the routed gate/up) are
-//     staged in LDS as bf16, XOR-swizzled by row so that the 32 rows one
-//     matrix-core operand read touches fall in distinct banks;
+// Kernel design (gfx950).  One work item = up to 128 rows of one expert (the
+// 128-row work map written by the routing, or 128 tokens for the shared
+// expert) x one block of output columns.  A work group has 8 waves (two per
+// SIMD).  Per K chunk of 128 (two quantisation groups):
+//   - the activation rows are staged in LDS as bf16, XOR-swizzled by row so
+//     that the 32 rows one matrix-core operand read touches fall in distinct
+//     banks;
 //   - each lane streams 2 x 16 contiguous bytes of one weight row straight
 //     from HBM (lane n%32 <-> row n; the two halves of the wave take adjacent
 //     16-byte pieces, so one load instruction covers 32 contiguous bytes of
-//     each of 32 rows) and dequantises them in registers into the B operand
-//     of v_mfma_f32_32x32x16_bf16: eight consecutive k of one column are
+//     each of 32 rows) and dequantises them in registers into the first
+//     operand of v_mfma_f32_32x32x16_bf16: eight consecutive k of one row are
 //     exactly one packed 32-bit word of codes.  The bf16 weights exist only in
 //     VGPRs and each is dequantised once per work item, then reused for all
 //     (up to four) 32-row M-subtiles;
-//   - the weight stream runs kStages chunks deep in registers (three chunks
-//     in flight while one is consumed) so that enough bytes are outstanding
-//     per CU to keep HBM busy; the activation tile is double buffered in LDS
-//     with its next chunk prefetched into registers (one barrier per chunk).
-// SiLU(gate)*up pairs gate wave w with up wave w+4 through LDS at the end.
+//   - the weight stream runs several chunks deep in registers so that enough
+//     bytes are outstanding per CU to keep HBM busy.
 #include "internal.h"
 
 namespace q4moe {
 
 constexpr int kKC = 128;               // K per chunk
 constexpr int kMT = kTileRows;         // rows per work item
-constexpr int kMT2 = 64;               // token rows per shared-down + combine item
 constexpr int kSlots = kKC / 8;        // 16-byte slots per staged row
 constexpr int kRowBytes = kKC * 2;     // bytes per staged row
 constexpr int kTileBytes = kMT * kRowBytes;
@@ -50,8 +45,6 @@ constexpr int kStages = 4;             // weight chunks held in registers
 constexpr int kALoads = kMT * kSlots / kThreads;
 static_assert(kMT * kSlots % kThreads == 0, "A tile split");
 
-enum { kGateUp = 0, kDownRouted = 1, kDownSharedCombine = 2 };
-
 template <int N>
 struct Int {
     static constexpr int value = N;
@@ -59,6 +52,61 @@ struct Int {
 
 __device__ __forceinline__ int lds_off(int row, int slot) {
     return row * kRowBytes + ((slot ^ (row & 15)) << 4);
+}
+
+
+// ---------------------------------------------------------------------------
+// Down projections.  Work items [0, sh_items) are the shared expert's 128-token
+// tiles, items [sh_items, sh_items + tile_bound) the routed 128-row work map
+// (entries at or past *n_tiles are empty).  The shared tiles come first so
+// that the fullest items start first.
+// ---------------------------------------------------------------------------
+struct DownItem {
+    int e, row0, M, shared;
+};
+
+__device__ __forceinline__ bool down_item(const PrefillArgs& a, int item, int sh_items, DownItem& it) {
+    if (item < sh_items) {
+        it.e = 0;
+        it.shared = 1;
+        it.row0 = item * kMT;
+        it.M = min(kMT, a.T - it.row0);
+        return true;
+    }
+    item -= sh_items;
+    if (item >= *a.n_tiles) return false;
+    it.e = a.tile_map[2 * item];
+    it.row0 = a.tile_map[2 * item + 1];
+    it.M = min(kMT, a.offsets[it.e + 1] - it.row0);
+    it.shared = 0;
+    return true;
+}
+
+// The dequantised weights are the first MFMA operand, so the 32x32 output
+// tile is (weight row n) x (activation row): lane l holds activation row
+// l % 32 of its subtile and, in elements 4g..4g+3, the four consecutive
+// weight rows n = 8g + 4*(l/32) + 0..3.  Outputs leave in groups of four
+// consecutive columns: fp16 (8 bytes) into the routed outputs `part` (row =
+// assignment), fp32 (16 bytes) into the shared expert's `sh_out` (row = token).
+__device__ __forceinline__ void down_store(const PrefillArgs& a, int shared, int dst, int n_lane,
+                                           const f32x16& acc) {
+    if (shared) {
+        float* srow = a.sh_out + (size_t)dst * a.d + n_lane;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 v = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+            *(f32x4*)(srow + 8 * g) = v;
+        }
+    } else {
+        uint16_t* prow = a.part + (size_t)dst * a.d + n_lane;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint2 v;
+            v.x = (uint32_t)f32_to_f16(acc[4 * g]) | ((uint32_t)f32_to_f16(acc[4 * g + 1]) << 16);
+            v.y = (uint32_t)f32_to_f16(acc[4 * g + 2]) | ((uint32_t)f32_to_f16(acc[4 * g + 3]) << 16);
+            *(uint2*)(prow + 8 * g) = v;
+        }
+    }
 }
 
 // One lane's share of one weight chunk: k in [kc + 32h, +32) (group kc/64)
@@ -71,11 +119,15 @@ struct BChunk {
     uint32_t s0, b0, s1, b1;
 };
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void expert_gemm_kernel(const PrefillArgs a, const int n_items,
-                                                               const int n_cb, const int n_wg) {
+// Any inter (a multiple of 64): the activation tile streams through LDS one
+// K-chunk at a time, double buffered, one barrier per chunk; each wave owns
+// 32 output columns of a 256-column block.
+__global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArgs a,
+                                                                const int sh_items,
+                                                                const int n_items, const int n_cb,
+                                                                const int n_wg) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
-    __shared__ int s_src[kMT];  // source row of the A operand per tile row (-1: none)
+    __shared__ int s_src[kMT];  // activation row per tile row (-1: none)
     __shared__ int s_dst[kMT];  // output row per tile row
 
     // XCD-aware order: consecutive logical indices (the column blocks of one
@@ -84,70 +136,30 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(const PrefillArgs
     const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
     const int item = L / n_cb, cb = L - item * n_cb;
     if (item >= n_items) return;
+    DownItem it;
+    if (!down_item(a, item, sh_items, it)) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-    int e = 0, row0, M;
-    bool shared_item = false;
-    const uint16_t* A;
-    int K, Nw, lda;
-    Q4 W;
-    // wave -> (matrix, 32-column block inside the work group)
-    const int mat = MODE == kGateUp ? (wave >> 2) : 0;
-    const int wcb = MODE == kGateUp ? (wave & 3) : wave;
-    const int cols_per_wg = MODE == kGateUp ? 128 : 256;
-    if (MODE == kGateUp) {
-        K = a.d; Nw = a.I; lda = a.d; A = a.x;
-        if (item < a.tile_bound) {
-            if (item >= *a.n_tiles) return;
-            e = a.tile_map[2 * item];
-            row0 = a.tile_map[2 * item + 1];
-            M = min(kMT, a.offsets[e + 1] - row0);
-            W = mat ? a.up : a.gate;
-        } else {
-            row0 = (item - a.tile_bound) * kMT;
-            M = min(kMT, a.T - row0);
-            shared_item = true;
-            W = mat ? a.sh_up : a.sh_gate;
-        }
-    } else if (MODE == kDownRouted) {
-        K = a.I; Nw = a.d; lda = a.I; A = a.h;
-        if (item >= *a.n_tiles) return;
-        e = a.tile_map[2 * item];
-        row0 = a.tile_map[2 * item + 1];
-        M = min(kMT, a.offsets[e + 1] - row0);
-        W = a.down;
-    } else {
-        K = a.I; Nw = a.d; lda = a.I; A = a.h_sh;
-        row0 = item * kMT2;
-        M = min(kMT2, a.T - row0);
-        W = a.sh_down;
-    }
+    const int K = a.I, Nw = a.d;
+    const uint16_t* A = it.shared ? a.h_sh : a.h;
+    const Q4 W = it.shared ? a.sh_down : a.down;
     if (tid < kMT) {
         int src = -1, dst = -1;
-        if (tid < M) {
-            const int r = row0 + tid;
-            if (MODE == kGateUp) {
-                src = shared_item ? r : a.perm[r] / a.k;
-                dst = r;
-            } else if (MODE == kDownRouted) {
-                src = r;
-                dst = a.perm[r];
-            } else {
-                src = r;
-                dst = r;
-            }
+        if (tid < it.M) {
+            src = it.row0 + tid;
+            dst = it.shared ? src : a.perm[src];
         }
         s_src[tid] = src;
         s_dst[tid] = dst;
     }
     __syncthreads();
 
-    const int n_ms = (M + 31) >> 5;  // active 32-row subtiles
-    const int wcol0 = cb * cols_per_wg + 32 * wcb;
+    const int n_ms = (it.M + 31) >> 5;  // active 32-row subtiles
+    const int wcol0 = cb * 256 + 32 * wave;
     const bool wave_on = wcol0 < Nw;
-    const int col = wcol0 + (lane & 31);  // this lane's output column
+    const int col = wcol0 + (lane & 31);  // this lane's weight row
     const int n_chunks = (K + kKC - 1) / kKC;
-    const size_t wrow = (size_t)e * Nw + (wave_on ? col : 0);  // weight row (matrix e, row col)
+    const size_t wrow = (size_t)it.e * Nw + (wave_on ? col : 0);
 
     u32x4 ast[kStages][kALoads];  // activation chunks in flight (same depth as the weights)
     BChunk bst[kStages];
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(const PrefillArgs
             const int slot = (tid + kThreads * p) & 15;
             const int kcol = c * kKC + 8 * slot;
             const int src = src_row[p];
-            const size_t off = (size_t)(src >= 0 ? src : 0) * lda + (kcol < K ? kcol : 0);
+            const size_t off = (size_t)(src >= 0 ? src : 0) * K + (kcol < K ? kcol : 0);
             areg[p] = *(const u32x4*)(A + off);
         }
     };
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(const PrefillArgs
         }
     };
     auto load_b = [&](int c, BChunk& st) {
-        const int kc0 = c * kKC < K ? c * kKC : 0;            // clamped: always a valid chunk
+        const int kc0 = c * kKC < K ? c * kKC : 0;  // clamped: always a valid chunk
         const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
         const uint32_t* qrow = W.q + wrow * (K / 8) + 4 * half;
         const size_t grow = wrow * (K / kGroup);
@@ -218,6 +230,8 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(const PrefillArgs
                 for (int ms = 0; ms < NMS; ++ms)
                     Anxt[ms] = *(const bf16x8*)(tile + lds_off(32 * ms + arow, slot));
             }
+            // keep the reads of step j+1 ahead of step j's matrix-core work
+            __builtin_amdgcn_sched_barrier(0);
             const bf16x8 B = j < 4 ? dequant8(st.lo[j & 3], s0, b0) : dequant8(st.hi[j & 3], s1, b1);
 #pragma unroll
             for (int ms = 0; ms < NMS; ++ms)
@@ -259,115 +273,513 @@ __global__ __launch_bounds__(kThreads) void expert_gemm_kernel(const PrefillArgs
         default: main_loop(Int<4>{}); break;
     }
 
-    // The dequantised weights are the first MFMA operand, so the 32x32 output
-    // tile is (weight row n) x (activation row): lane l holds activation row
-    // l % 32 of its subtile and, in elements 4g..4g+3, the four consecutive
-    // weight rows n = 8g + 4*(l/32) + 0..3.  Outputs therefore leave as
-    // 8-byte groups of four columns.
-    const int n_lane = wcol0 + 4 * half;  // + 8g
-    if (MODE == kGateUp) {
-        float* xch = (float*)lds;  // gate accumulators: [4 col blocks][4 subtiles][16][64 lanes]
-        __syncthreads();
-        if (mat == 0 && wave_on) {
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
-                if (ms < n_ms)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) xch[((wcb * 4 + ms) * 16 + i) * 64 + lane] = acc[ms][i];
-        }
-        __syncthreads();
-        if (mat == 0 || !wave_on) return;
-        uint16_t* out = shared_item ? a.h_sh : a.h;
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) {
-            const int row = 32 * ms + (lane & 31);
-            if (ms >= n_ms || row >= M) continue;
-            uint16_t* orow = out + (size_t)s_dst[row] * a.I + n_lane;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float hv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float gate = xch[((wcb * 4 + ms) * 16 + 4 * g + r) * 64 + lane];
-                    hv[r] = silu(gate) * acc[ms][4 * g + r];
-                }
-                uint2 v;
-                v.x = pack_bf16x2(hv[0], hv[1]);
-                v.y = pack_bf16x2(hv[2], hv[3]);
-                *(uint2*)(orow + 8 * g) = v;
-            }
-        }
-        return;
-    }
     if (!wave_on) return;
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
         const int row = 32 * ms + (lane & 31);
-        if (ms >= n_ms || row >= M) continue;
-        const int dst = s_dst[row];
-        if (MODE == kDownRouted) {
-            uint16_t* prow = a.part + (size_t)dst * a.d + n_lane;
+        if (ms >= n_ms || row >= it.M) continue;
+        down_store(a, it.shared, s_dst[row], wcol0 + 4 * half, acc[ms]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Down projection with the activation tile resident in LDS (inter in
+// (384, 512], four K-chunks).  The whole M x inter bf16 tile of a work item
+// is loaded into LDS once behind a single barrier; then every wave streams
+// its weights through kDnBlocks blocks of 256 output columns x 4 K-chunks as
+// one continuous register pipeline (three chunks in flight), writing each
+// column block as soon as its last chunk is done.  No barrier sits in the
+// main loop.
+// ---------------------------------------------------------------------------
+constexpr int kDnMaxI = 512;
+constexpr int kDnBlocks = 4;  // 256-column blocks per work group
+
+__global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillArgs a,
+                                                                 const int sh_items,
+                                                                 const int n_items, const int n_cb,
+                                                                 const int n_wg) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kMT * kDnMaxI * 2];
+    __shared__ int s_dst[kMT];
+
+    const int b = blockIdx.x;
+    const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
+    const int item = L / n_cb, cb = L - item * n_cb;
+    if (item >= n_items) return;
+    DownItem it;
+    if (!down_item(a, item, sh_items, it)) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int K = a.I, Nw = a.d;
+    const int M = it.M, row0 = it.row0;
+    const uint16_t* A = it.shared ? a.h_sh : a.h;
+    const Q4 W = it.shared ? a.sh_down : a.down;
+    constexpr int nk = kStages;  // K-chunks per column block
+    constexpr int row_bytes = nk * kRowBytes;
+    if (tid < kMT) s_dst[tid] = tid < M ? (it.shared ? row0 + tid : a.perm[row0 + tid]) : -1;
+
+    const int n_ms = (M + 31) >> 5;
+    constexpr int nq = kDnBlocks * nk;  // chunks this wave streams
+    auto wcol0_of = [&](int blk) { return cb * (256 * kDnBlocks) + 256 * blk + 32 * wave; };
+    auto load_b = [&](int q, BChunk& st) {
+        const int qq = q < nq ? q : nq - 1;  // clamped: always a valid chunk
+        const int blk = qq / nk, c = qq - blk * nk;
+        const int wc = wcol0_of(blk);
+        const size_t wrow = (size_t)it.e * Nw + (wc < Nw ? wc + (lane & 31) : 0);
+        const int kc0 = c * kKC < K ? c * kKC : 0;
+        const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
+        const uint32_t* qrow = W.q + wrow * (K / 8) + 4 * half;
+        const size_t grow = wrow * (K / kGroup);
+        st.lo = *(const u32x4*)(qrow + kc0 / 8);
+        st.hi = *(const u32x4*)(qrow + kc1 / 8);
+        st.s0 = W.scale[grow + kc0 / kGroup];
+        st.b0 = W.bias[grow + kc0 / kGroup];
+        st.s1 = W.scale[grow + kc1 / kGroup];
+        st.b1 = W.bias[grow + kc1 / kGroup];
+    };
+    BChunk bst[kStages];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 v;
-                v.x = (uint32_t)f32_to_f16(acc[ms][4 * g]) | ((uint32_t)f32_to_f16(acc[ms][4 * g + 1]) << 16);
-                v.y = (uint32_t)f32_to_f16(acc[ms][4 * g + 2]) | ((uint32_t)f32_to_f16(acc[ms][4 * g + 3]) << 16);
-                *(uint2*)(prow + 8 * g) = v;
+    for (int u = 0; u < kStages - 1; ++u) load_b(u, bst[u]);
+
+    // resident activation tile: row r, 16-byte slot s at r * row_bytes + ((s ^ (r & 15)) << 4);
+    // rows past M and columns past K are zero
+    {
+        constexpr int slots = nk * kSlots;  // 16-byte slots per row (K padded to the chunk)
+        constexpr int total = kMT * slots;
+        static_assert(total % (kThreads * 4) == 0, "resident tile split");
+        for (int i0 = 0; i0 < total; i0 += kThreads * 4) {
+            u32x4 v[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int i = i0 + tid + kThreads * p;
+                const int row = i / slots, slot = i - row * slots;
+                const int kcol = 8 * slot;
+                const bool ok = row < M && kcol < K;
+                const size_t off = (size_t)(ok ? row0 + row : 0) * K + (ok ? kcol : 0);
+                v[p] = *(const u32x4*)(A + off);
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                v[p] = ok ? v[p] : z;
             }
-        } else {
-            // fixed order: routed slots 0..k-1 with their scores, then the shared expert
-            const uint16_t* pr = a.part + (size_t)dst * a.k * a.d + n_lane;
-            const float* wt = a.topk_w + (size_t)dst * a.k;
-            float ws[kMaxTopK];
-            uint2 pv[kMaxTopK][4];
 #pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s) {
-                const int ss = s < a.k ? s : 0;  // loads stay unconditional
-                ws[s] = wt[ss];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) pv[s][g] = *(const uint2*)(pr + (size_t)ss * a.d + 8 * g);
+            for (int p = 0; p < 4; ++p) {
+                const int i = i0 + tid + kThreads * p;
+                const int row = i / slots, slot = i - row * slots;
+                *(u32x4*)(lds + row * row_bytes + ((slot ^ (row & 15)) << 4)) = v[p];
             }
-            uint16_t* yrow = a.y + (size_t)dst * a.d + n_lane;
+        }
+    }
+    __syncthreads();
+
+    f32x16 acc[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+
+    auto epilogue = [&](int blk) __attribute__((always_inline)) {
+        const int wc = wcol0_of(blk);
+        if (wc < Nw) {
 #pragma unroll
-                for (int s = 0; s < kMaxTopK; ++s) {
-                    if (s < a.k) {
-                        yv[0] += ws[s] * f16_to_f32(pv[s][g].x & 0xFFFFu);
-                        yv[1] += ws[s] * f16_to_f32(pv[s][g].x >> 16);
-                        yv[2] += ws[s] * f16_to_f32(pv[s][g].y & 0xFFFFu);
-                        yv[3] += ws[s] * f16_to_f32(pv[s][g].y >> 16);
+            for (int ms = 0; ms < 4; ++ms) {
+                const int row = 32 * ms + (lane & 31);
+                if (ms >= n_ms || row >= M) continue;
+                down_store(a, it.shared, s_dst[row], wc + 4 * half, acc[ms]);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+    };
+
+    auto compute = [&](auto nms_tag, int c, const BChunk& st) {
+        constexpr int NMS = decltype(nms_tag)::value;
+        const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
+        const float s0 = ok0 ? bf16_to_f32(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
+        const float s1 = ok1 ? bf16_to_f32(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
+        const int arow = lane & 31, sbase = c * kSlots;
+        auto aread = [&](int ms, int slot) {
+            const int row = 32 * ms + arow;
+            return *(const bf16x8*)(lds + row * row_bytes + (((sbase + slot) ^ (row & 15)) << 4));
+        };
+        bf16x8 Acur[NMS], Anxt[NMS];
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms) Acur[ms] = aread(ms, 4 * half);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < 7) {
+                const int slot = (j + 1 < 4 ? 0 : 8) + 4 * half + ((j + 1) & 3);
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) Anxt[ms] = aread(ms, slot);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 B = j < 4 ? dequant8(st.lo[j & 3], s0, b0) : dequant8(st.hi[j & 3], s1, b1);
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+                acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B, Acur[ms], acc[ms], 0, 0, 0);
+            if (j < 7) {
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) Acur[ms] = Anxt[ms];
+            }
+        }
+    };
+
+    // chunk u of every column block uses stage u, so the block loop needs no
+    // remainder handling and each column block's outputs are written once,
+    // outside the unrolled body
+    auto main_loop = [&](auto nms_tag) {
+        for (int blk = 0; blk < kDnBlocks; ++blk) {
+#pragma unroll
+            for (int u = 0; u < kStages; ++u) {
+                load_b(blk * kStages + u + kStages - 1, bst[(u + kStages - 1) % kStages]);
+                if (wcol0_of(blk) < Nw) compute(nms_tag, u, bst[u]);
+            }
+            epilogue(blk);
+        }
+    };
+    switch (n_ms) {
+        case 1: main_loop(Int<1>{}); break;
+        case 2: main_loop(Int<2>{}); break;
+        case 3: main_loop(Int<3>{}); break;
+        default: main_loop(Int<4>{}); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent gate/up GEMM.  One work group per CU walks a static list of
+// units (work item, 128-intermediate-column block): unit u = g, g + G, ...
+// where G is the grid size.  Units are numbered so that the column blocks of
+// one item have the same index modulo 8 and therefore run on one XCD (work
+// groups are dispatched to the 8 XCDs round-robin), sharing its L2 for the
+// gathered activation rows.  The descriptors (expert, rows, source and
+// destination rows) of up to kBatch units are computed once up front, and
+// the K-chunk pipeline then runs continuously from one unit into the next,
+// so no per-item start-up (dependent index loads) or pipeline fill/drain is
+// paid per item.
+//
+// Each wave owns 16 intermediate columns j0..j0+15: the 32 weight rows of its
+// MFMA operand are gate rows j0..j0+15 (lanes 0-15) and up rows j0..j0+15
+// (lanes 16-31).  In the 32x32 output tile a lane then holds gate row r and
+// up row r + 16 of the same token in elements i and i + 8, so SiLU(gate)*up
+// needs no data exchange.
+// Weights stream three chunks ahead and activations two (activations of the
+// chunk two ahead are issued before the weights of the chunk three ahead, so
+// waiting for an activation chunk never waits for younger weight loads).
+// ---------------------------------------------------------------------------
+constexpr int kBatch = 8;
+
+struct UnitDesc {
+    int e, row0, M, cb, shared;
+};
+
+// A unit descriptor read back from LDS, moved to scalar registers: every
+// field is uniform across the work group.
+__device__ __forceinline__ UnitDesc uniform_desc(const UnitDesc& d) {
+    UnitDesc u;
+    u.e = __builtin_amdgcn_readfirstlane(d.e);
+    u.row0 = __builtin_amdgcn_readfirstlane(d.row0);
+    u.M = __builtin_amdgcn_readfirstlane(d.M);
+    u.cb = __builtin_amdgcn_readfirstlane(d.cb);
+    u.shared = __builtin_amdgcn_readfirstlane(d.shared);
+    return u;
+}
+
+// One lane's share of one weight chunk with the scale and bias of both
+// groups packed as pairs (low half = the group of lo, high half = hi).
+struct WChunk {
+    u32x4 lo, hi;
+    uint32_t sp, bp;
+};
+
+__global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, const int n_cb) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
+    __shared__ UnitDesc s_unit[kBatch];
+    __shared__ int s_src[kBatch][kMT];
+    __shared__ int s_dst[kBatch][kMT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int G = gridDim.x, g = blockIdx.x;
+    const int K = a.d, Nw = a.I;
+    const int n_tiles = *a.n_tiles;
+    const int sh_items = (a.T + kMT - 1) / kMT;
+    const int n_items = n_tiles + sh_items;
+    const int n_units = (n_items + 7) / 8 * 8 * n_cb;
+    const int NL = ((K + kKC - 1) / kKC + kStages - 1) / kStages * kStages;  // chunks per unit
+    const bool pair_sb = (K / kGroup) % 2 == 0;  // scale/bias pairs are 4-byte aligned
+    const bool is_up = (lane & 16) != 0;         // weight row lane%32: gate j0+n or up j0+n-16
+    const int jrow = lane & 15;
+
+    f32x16 acc[4];
+    WChunk bst[kStages];
+    u32x4 ast[kStages][kALoads];
+
+    int u_next = g;
+    while (true) {
+        // ---- descriptors of up to kBatch valid units ----
+        __syncthreads();  // the previous batch is done with s_unit / s_src / s_dst
+        int nb = 0;
+        while (nb < kBatch && u_next < n_units) {
+            const int blk = u_next / (8 * n_cb), r = u_next - blk * 8 * n_cb;
+            const int cb = r >> 3, item = blk * 8 + (r & 7);
+            u_next += G;
+            if (item >= n_items) continue;
+            const int bi = nb++;
+            int e = 0, row0, M, shared = 0;
+            if (item < n_tiles) {
+                e = a.tile_map[2 * item];
+                row0 = a.tile_map[2 * item + 1];
+                M = min(kMT, a.offsets[e + 1] - row0);
+            } else {
+                shared = 1;
+                row0 = (item - n_tiles) * kMT;
+                M = min(kMT, a.T - row0);
+            }
+            if (tid == 0) s_unit[bi] = UnitDesc{e, row0, M, cb, shared};
+            if (tid < kMT) {
+                int src = 0, dst = -1;
+                if (tid < M) {
+                    src = shared ? row0 + tid : a.perm[row0 + tid] / a.k;
+                    dst = row0 + tid;
+                }
+                s_src[bi][tid] = src;
+                s_dst[bi][tid] = dst;
+            }
+        }
+        if (nb == 0) break;
+        __syncthreads();
+
+        // ---- loaders (clamped to valid addresses, never under a branch) ----
+        // Rows past M were given source row 0 in the descriptor (their products
+        // are never stored), and columns at or past K read column 0 of the row
+        // (their weights are zeroed in compute), so every load stays inside x.
+        // The column slot is the same for the kALoads loads of a lane.
+        auto load_a = [&](int sp, u32x4 (&areg)[kALoads]) {
+            sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
+            const int bb = sp / NL, c = sp - bb * NL;
+            const int kc = c * kKC + 8 * (tid & 15);
+            const uint32_t col = kc < K ? (uint32_t)kc : 0u;
+#pragma unroll
+            for (int p = 0; p < kALoads; ++p) {
+                const int row = (tid + kThreads * p) >> 4;
+                const uint32_t off = (uint32_t)s_src[bb][row] * (uint32_t)K + col;
+                areg[p] = *(const u32x4*)(a.x + off);
+            }
+        };
+        auto load_b = [&](int sp, WChunk& st) {
+            sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
+            const int bb = sp / NL, c = sp - bb * NL;
+            const UnitDesc ud = uniform_desc(s_unit[bb]);
+            const Q4 Wg = ud.shared ? a.sh_gate : a.gate;
+            const Q4 Wu = ud.shared ? a.sh_up : a.up;
+            const int j0 = ud.cb * 128 + 16 * wave;
+            const size_t wrow = (size_t)ud.e * Nw + (j0 < Nw ? j0 + jrow : 0);
+            const uint32_t* qb = is_up ? Wu.q : Wg.q;
+            const uint16_t* sb = is_up ? Wu.scale : Wg.scale;
+            const uint16_t* bbp = is_up ? Wu.bias : Wg.bias;
+            const int kc0 = c * kKC < K ? c * kKC : 0;
+            const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
+            const uint32_t* qrow = qb + wrow * (K / 8) + 4 * half;
+            const size_t gi = wrow * (K / kGroup) + kc0 / kGroup;
+            st.lo = *(const u32x4*)(qrow + kc0 / 8);
+            st.hi = *(const u32x4*)(qrow + kc1 / 8);
+            if (pair_sb) {
+                st.sp = *(const uint32_t*)(sb + gi);
+                st.bp = *(const uint32_t*)(bbp + gi);
+            } else {  // odd group count: two 2-byte loads each
+                const size_t g1 = wrow * (K / kGroup) + kc1 / kGroup;
+                st.sp = (uint32_t)sb[gi] | ((uint32_t)sb[g1] << 16);
+                st.bp = (uint32_t)bbp[gi] | ((uint32_t)bbp[g1] << 16);
+            }
+        };
+        auto store_a = [&](int buf, const u32x4 (&areg)[kALoads]) {
+#pragma unroll
+            for (int p = 0; p < kALoads; ++p) {
+                const int i = tid + kThreads * p, row = i >> 4, slot = i & 15;
+                *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = areg[p];
+            }
+        };
+        auto compute = [&](auto nms_tag, int c, int buf, const WChunk& st) {
+            constexpr int NMS = decltype(nms_tag)::value;
+            const unsigned char* tile = lds + buf * kTileBytes;
+            const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
+            const float s0 = ok0 ? bf16_to_f32(st.sp & 0xFFFFu) : 0.0f;
+            const float b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
+            const float s1 = ok1 ? bf16_to_f32(st.sp >> 16) : 0.0f;
+            const float b1 = ok1 ? bf16_to_f32(st.bp >> 16) : 0.0f;
+            // row 32*ms + lane%32 has (row & 15) == (lane & 15) for every ms, so the
+            // swizzled slot offset is shared by the subtiles
+            const unsigned char* trow = tile + (lane & 31) * kRowBytes;
+            const int sw = lane & 15;
+            bf16x8 Acur[NMS], Anxt[NMS];
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+                Acur[ms] = *(const bf16x8*)(trow + 32 * ms * kRowBytes + (((4 * half) ^ sw) << 4));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < 7) {
+                    const int slot = (j + 1 < 4 ? 0 : 8) + 4 * half + ((j + 1) & 3);
+                    const int so = (slot ^ sw) << 4;
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms)
+                        Anxt[ms] = *(const bf16x8*)(trow + 32 * ms * kRowBytes + so);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const bf16x8 B =
+                    j < 4 ? dequant8(st.lo[j & 3], s0, b0) : dequant8(st.hi[j & 3], s1, b1);
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms)
+                    acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B, Acur[ms], acc[ms], 0, 0, 0);
+                if (j < 7) {
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms) Acur[ms] = Anxt[ms];
+                }
+            }
+        };
+        // h = bf16(SiLU(gate) * up): elements i (gate row) and i + 8 (up row)
+        auto epilogue = [&](int bb) {
+            const UnitDesc ud = uniform_desc(s_unit[bb]);
+            const int n_ms = (ud.M + 31) >> 5;
+            const int j0 = ud.cb * 128 + 16 * wave;
+            if (j0 < Nw) {
+                uint16_t* out = ud.shared ? a.h_sh : a.h;
+#pragma unroll
+                for (int ms = 0; ms < 4; ++ms) {
+                    const int row = 32 * ms + (lane & 31);
+                    if (ms >= n_ms || row >= ud.M) continue;
+                    uint16_t* orow = out + (size_t)s_dst[bb][row] * a.I + j0 + 4 * half;
+#pragma unroll
+                    for (int gq = 0; gq < 2; ++gq) {
+                        float hv[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            hv[r] = silu(acc[ms][4 * gq + r]) * acc[ms][8 + 4 * gq + r];
+                        uint2 v;
+                        v.x = pack_bf16x2(hv[0], hv[1]);
+                        v.y = pack_bf16x2(hv[2], hv[3]);
+                        *(uint2*)(orow + 8 * gq) = v;
                     }
                 }
-                uint2 v;
-                v.x = pack_bf16x2(yv[0] + acc[ms][4 * g], yv[1] + acc[ms][4 * g + 1]);
-                v.y = pack_bf16x2(yv[2] + acc[ms][4 * g + 2], yv[3] + acc[ms][4 * g + 3]);
-                *(uint2*)(yrow + 8 * g) = v;
             }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+        };
+        auto unit_loop = [&](auto nms_tag, int bb) {
+            const int cbu = __builtin_amdgcn_readfirstlane(s_unit[bb].cb);
+            const bool on = cbu * 128 + 16 * wave < Nw;
+            for (int c0 = 0; c0 < NL; c0 += kStages) {
+#pragma unroll
+                for (int u = 0; u < kStages; ++u) {
+                    const int c = c0 + u, sp = bb * NL + c;
+                    store_a(u & 1, ast[u]);
+                    __syncthreads();
+                    load_a(sp + 2, ast[(u + 2) % kStages]);
+                    load_b(sp + 3, bst[(u + 3) % kStages]);
+                    if (on) compute(nms_tag, c, u & 1, bst[u]);
+                }
+            }
+        };
+
+        // ---- the batch: one continuous pipeline over nb units ----
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+        load_a(0, ast[0]);
+        load_a(1, ast[1]);
+#pragma unroll
+        for (int u = 0; u < kStages - 1; ++u) load_b(u, bst[u]);
+        for (int bb = 0; bb < nb; ++bb) {
+            switch ((__builtin_amdgcn_readfirstlane(s_unit[bb].M) + 31) >> 5) {
+                case 1: unit_loop(Int<1>{}, bb); break;
+                case 2: unit_loop(Int<2>{}, bb); break;
+                case 3: unit_loop(Int<3>{}, bb); break;
+                default: unit_loop(Int<4>{}, bb); break;
+            }
+            epilogue(bb);
         }
     }
 }
 
-template <int MODE>
-static hipError_t launch_gemm(const PrefillArgs& a, int n_items, int n_cols, int cols_per_wg,
-                              hipStream_t s) {
-    const int n_cb = (n_cols + cols_per_wg - 1) / cols_per_wg;
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+static hipError_t launch_gate_up(const PrefillArgs& a, hipStream_t s) {
+    const int n_cb = (a.I + 127) / 128;
+    const int sh_items = (a.T + kMT - 1) / kMT;
+    const int max_units = (a.tile_bound + sh_items + 7) / 8 * 8 * n_cb;
+    int grid = device_cus();
+    if (grid > max_units) grid = max_units;
+    hipLaunchKernelGGL(gate_up_kernel, dim3(grid), dim3(kThreads), 0, s, a, n_cb);
+    trace_point(s);
+    return hipGetLastError();
+}
+
+static hipError_t launch_down(const PrefillArgs& a, hipStream_t s) {
+    const int sh_items = (a.T + kMT - 1) / kMT;
+    const int n_items = sh_items + a.tile_bound;
+    const bool resident = (a.I + kKC - 1) / kKC == kStages;
+    const int cols_per_wg = resident ? 256 * kDnBlocks : 256;
+    const int n_cb = (a.d + cols_per_wg - 1) / cols_per_wg;
     const int n_wg = ((n_items * n_cb) + 7) & ~7;
-    if (n_wg > 0)
-        hipLaunchKernelGGL((expert_gemm_kernel<MODE>), dim3(n_wg), dim3(kThreads), 0, s, a,
+    if (resident)
+        hipLaunchKernelGGL(down_resident_kernel, dim3(n_wg), dim3(kThreads), 0, s, a, sh_items,
+                           n_items, n_cb, n_wg);
+    else
+        hipLaunchKernelGGL(down_chunked_kernel, dim3(n_wg), dim3(kThreads), 0, s, a, sh_items,
                            n_items, n_cb, n_wg);
     trace_point(s);
     return hipGetLastError();
 }
 
+// y_t = bf16( sum_{s<k} w[t,s] * part[t*k+s] + sh_out[t] ): the k routed
+// outputs in slot order, then the shared expert, all in fp32.  One work group
+// per token; each thread owns 8 consecutive columns, so every load is 16 or 32
+// contiguous bytes per lane and a wave reads whole 1 KB spans.
+__global__ __launch_bounds__(256) void combine_kernel(const PrefillArgs a) {
+    const int t = blockIdx.x, d = a.d, k = a.k;
+    float w[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) w[s] = a.topk_w[(size_t)t * k + (s < k ? s : 0)];
+    const uint16_t* pt = a.part + (size_t)t * k * d;
+    const float* st = a.sh_out + (size_t)t * d;
+    for (int c = 8 * (int)threadIdx.x; c < d; c += 8 * 256) {
+        u32x4 p[kMaxTopK];
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) p[s] = *(const u32x4*)(pt + (size_t)(s < k ? s : 0) * d + c);
+        const f32x4 sh0 = *(const f32x4*)(st + c);
+        const f32x4 sh1 = *(const f32x4*)(st + c + 4);
+        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (s < k) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += w[s] * f16_to_f32(p[s][i] & 0xFFFFu);
+                    acc[2 * i + 1] += w[s] * f16_to_f32(p[s][i] >> 16);
+                }
+            }
+        }
+        u32x4 out;
+        out[0] = pack_bf16x2(acc[0] + sh0[0], acc[1] + sh0[1]);
+        out[1] = pack_bf16x2(acc[2] + sh0[2], acc[3] + sh0[3]);
+        out[2] = pack_bf16x2(acc[4] + sh1[0], acc[5] + sh1[1]);
+        out[3] = pack_bf16x2(acc[6] + sh1[2], acc[7] + sh1[3]);
+        *(u32x4*)(a.y + (size_t)t * d + c) = out;
+    }
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-    const int sh_items = (a.T + kMT - 1) / kMT;
-    hipError_t err = launch_gemm<kGateUp>(a, a.tile_bound + sh_items, a.I, 128, s);
+    hipError_t err = launch_gate_up(a, s);
     if (err != hipSuccess) return err;
-    err = launch_gemm<kDownRouted>(a, a.tile_bound, a.d, 256, s);
+    err = launch_down(a, s);
     if (err != hipSuccess) return err;
-    return launch_gemm<kDownSharedCombine>(a, (a.T + kMT2 - 1) / kMT2, a.d, 256, s);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+    trace_point(s);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -119,7 +119,8 @@ def test_workspace_bytes_cover_the_staged_buffers():
     for T, d, I, E, k in ((2048, 2048, 512, 256, 8), (32, 512, 128, 32, 4), (1, 2048, 512, 256, 8)):
         L = _layer(d, I, E, k)  # keep the struct alive across the call
         n = lib.moe_workspace_bytes(C.addressof(L), T)
-        staged = 2 * (T * k * I + T * I + T * k * d)  # h, shared h, fp16 expert outputs
+        # h, shared h, fp16 routed outputs, fp32 shared outputs
+        staged = 2 * (T * k * I + T * I + T * k * d) + 4 * T * d
         assert staged <= n <= staged + 2 * 4 * (d // 32) * E + 64 * 1024
     bad = _layer(d=100)
     assert lib.moe_workspace_bytes(C.addressof(bad), 16) == 0
