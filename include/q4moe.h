@@ -90,7 +90,10 @@ enum {
      scale [n_mat][N][K/64] bf16
      bias  [n_mat][N][K/64] bf16
    Row n of matrix m holds the weights that produce output n from the K
-   inputs; w(n, k) = q(n, k) * scale(n, k/64) + bias(n, k/64). */
+   inputs; w(n, k) = q(n, k) * scale(n, k/64) + bias(n, k/64), used as the
+   nearest bf16 value.  That rounding is exact (one rounding of the exact
+   affine value) for finite scales below 2^119 in magnitude whose exponent
+   lies within 12 of the bias's; the kernels do not check the data. */
 typedef struct {
     const uint32_t* q;
     const uint16_t* scale;

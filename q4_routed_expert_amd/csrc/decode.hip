@@ -114,9 +114,9 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(const DecodeArgs a)
                 gq[r] = *(const u32x4*)(G.q + row * (d / 8) + k0 / 8);
                 uq[r] = *(const u32x4*)(U.q + row * (d / 8) + k0 / 8);
                 const size_t gi = row * (d / kGroup) + k0 / kGroup;
-                gs[r] = bf16_to_f32(G.scale[gi]);
+                gs[r] = dq_scale(G.scale[gi]);
                 gb[r] = bf16_to_f32(G.bias[gi]);
-                us[r] = bf16_to_f32(U.scale[gi]);
+                us[r] = dq_scale(U.scale[gi]);
                 ub[r] = bf16_to_f32(U.bias[gi]);
             }
 #pragma unroll
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const DecodeArgs a) {
                 const size_t row = shared ? (size_t)n : (size_t)a.sel_idx[s] * d + n;
                 q[s] = *(const u32x4*)(D.q + row * (I / 8) + k0 / 8);
                 const size_t gi = row * (I / kGroup) + k0 / kGroup;
-                sc[s] = bf16_to_f32(D.scale[gi]);
+                sc[s] = dq_scale(D.scale[gi]);
                 bi[s] = bf16_to_f32(D.bias[gi]);
             }
         }

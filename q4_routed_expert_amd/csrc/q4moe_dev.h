@@ -56,43 +56,55 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// A group's scale as dequant8 takes it: scale * 2^9 (exact for |scale| < 2^119).
+__device__ __forceinline__ float dq_scale(uint32_t bf16_bits) {
+    return bf16_to_f32(bf16_bits) * 512.0f;
+}
+
 // Dequantise one 32-bit word of eight 4-bit codes (lowest nibble = lowest k)
-// with the group's scale s and bias b into eight bf16 weights in k order:
-// w = bf16(q * s + b).  q*s is exact in fp32 (at most 12 significant bits) and
-// so is the sum whenever the exponents of s and b lie within 12 of each other,
-// so the single fp32 fma followed by the round-to-nearest-even conversion
-// gives the nearest bf16 to the exact affine value.
+// with the group's scale and bias into eight bf16 weights in k order:
+// w = bf16(q * scale + bias).  s9 is scale * 2^9 (dq_scale).
 //
-// 23 VALU instructions per word: 3 to split the even and odd codes into the
-// four bytes of two words, 8 v_cvt_f32_ubyte{0..3} (each converts one byte in
-// place), 8 v_fma_f32 and 4 v_cvt_pk_bf16_f32.  The empty asm statements hide
-// the masks from known-bits analysis, which would otherwise turn each byte
-// read into a 4-bit extract plus a separate convert.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s, float b) {
-    uint32_t ev = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
-    uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-    asm("" : "+v"(ev));
-    asm("" : "+v"(od));
+// A byte holding a code q in 0..15, read as an fp8 e4m3 value (the OCP
+// format gfx950 converts: 3 mantissa bits, exponent bias 7), is exactly
+// q * 2^-9: codes 0..7 are the subnormals m * 2^-9 and codes 8..15 the first
+// normal binade (1 + m/8) * 2^-6 = (8 + m) * 2^-9.  So v_cvt_pk_f32_fp8 turns
+// two codes into two exact floats in one instruction, and
+// fma(q * 2^-9, scale * 2^9, bias) = fma(q, scale, bias): q * scale is exact in
+// fp32 (at most 12 significant bits) and so is the sum whenever the exponents
+// of scale and bias lie within 12 of each other; the single rounding of the
+// fma followed by the round-to-nearest-even conversion gives the nearest bf16
+// to the exact affine value.
+//
+// 19 VALU instructions per word: 3 to split the even and odd codes into the
+// four bytes of two words, 4 v_cvt_pk_f32_fp8, 8 v_fma_f32 and 4
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s9, float b) {
+    const uint32_t ev = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6 in bytes 0..3
+    const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+    const f32x2 e01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, false);  // q0, q2 (* 2^-9)
+    const f32x2 e23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)ev, true);   // q4, q6
+    const f32x2 o01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, false);  // q1, q3
+    const f32x2 o23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)od, true);   // q5, q7
     u32x4 r;
-    r[0] = pack_bf16x2(__builtin_fmaf((float)(ev & 0xFFu), s, b),
-                       __builtin_fmaf((float)(od & 0xFFu), s, b));
-    r[1] = pack_bf16x2(__builtin_fmaf((float)((ev >> 8) & 0xFFu), s, b),
-                       __builtin_fmaf((float)((od >> 8) & 0xFFu), s, b));
-    r[2] = pack_bf16x2(__builtin_fmaf((float)((ev >> 16) & 0xFFu), s, b),
-                       __builtin_fmaf((float)((od >> 16) & 0xFFu), s, b));
-    r[3] = pack_bf16x2(__builtin_fmaf((float)(ev >> 24), s, b),
-                       __builtin_fmaf((float)(od >> 24), s, b));
+    r[0] = pack_bf16x2(__builtin_fmaf(e01[0], s9, b), __builtin_fmaf(o01[0], s9, b));
+    r[1] = pack_bf16x2(__builtin_fmaf(e01[1], s9, b), __builtin_fmaf(o01[1], s9, b));
+    r[2] = pack_bf16x2(__builtin_fmaf(e23[0], s9, b), __builtin_fmaf(o23[0], s9, b));
+    r[3] = pack_bf16x2(__builtin_fmaf(e23[1], s9, b), __builtin_fmaf(o23[1], s9, b));
     return __builtin_bit_cast(bf16x8, r);
 }
 
-// acc + sum over the eight weights of one code word of bf16(q*s + b) * v, with
+// acc + sum over the eight weights of one code word of bf16(q*s + b) * v (s9 =
+// dq_scale of s), with
 // v the matching eight bf16 activations as four packed pairs in k order
 // (v_dot2_f32_bf16: both products and the sum in fp32).
 // (The activations are reinterpreted as one bf16x8 and split with shuffles:
 // a bit cast of each 32-bit element separately was compiled into four uses of
 // element 0.)
-__device__ __forceinline__ float dot8_bf16(uint32_t w, float s, float b, u32x4 v, float acc) {
-    const bf16x8 wv = dequant8(w, s, b);
+__device__ __forceinline__ float dot8_bf16(uint32_t w, float s9, float b, u32x4 v, float acc) {
+    const bf16x8 wv = dequant8(w, s9, b);
     const bf16x8 xv = __builtin_bit_cast(bf16x8, v);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 0, 1),
                                           __builtin_shufflevector(xv, xv, 0, 1), acc, false);

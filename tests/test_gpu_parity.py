@@ -132,6 +132,18 @@ def test_dequant_bit_exact(dev):
     b = np.array([[0x3F80]], np.uint16)
     got = q4.dequant(q4._dev(q, dev), q4._dev(s, dev), q4._dev(b, dev))
     assert np.array_equal(host_bits(got), oracle.dequant(q, s, b))
+    # wide ranges: scales from 2^-107 to 2^73 of either sign (and zero), biases
+    # within 2^+-10 of the scale, where q*scale + bias is exact in fp32
+    N, K = 64, 512
+    q = rng.integers(0, 1 << 32, size=(N, K // 8), dtype=np.uint32)
+    es = rng.integers(20, 200, size=(N, K // 64))
+    eb = np.clip(es + rng.integers(-10, 11, size=es.shape), 1, 254)
+    sign = lambda: rng.integers(0, 2, size=es.shape) << 15
+    s = (sign() | (es << 7) | rng.integers(0, 128, size=es.shape)).astype(np.uint16)
+    b = (sign() | (eb << 7) | rng.integers(0, 128, size=es.shape)).astype(np.uint16)
+    s[0, :] = 0
+    got = q4.dequant(q4._dev(q, dev), q4._dev(s, dev), q4._dev(b, dev))
+    assert np.array_equal(host_bits(got), oracle.dequant(q, s, b))
 
 
 # ------------------------------------------------------------------ workloads
