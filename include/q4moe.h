@@ -80,6 +80,10 @@ enum {
 #define MOE_BLOCK_ROWS 32
 #define MOE_TILE_ROWS 128
 
+/* moe_route counts assignments per block of this many consecutive tokens
+   (see moe_routing.blk_counts). */
+#define MOE_ROUTE_BLOCK 256
+
 /* moe_route flag: start from the logits already in routing->logits instead of
    computing them (used to route from given fp32 logits). */
 #define MOE_LOGITS_IN 1u
@@ -131,6 +135,8 @@ typedef struct {
     int32_t* n_blocks;  /* [1] */
     int32_t* tile_map;  /* [T*k/128 + E][2] (expert, first sorted row) per 128-row item */
     int32_t* n_tiles;   /* [1] */
+    int32_t* blk_counts;/* [ceil(T/MOE_ROUTE_BLOCK)][E] scratch of moe_route: per-block
+                           expert counts; contents unspecified afterwards */
 } moe_routing;
 
 /* Entries needed in block_map / tile_map for T tokens (pairs of int32). */
@@ -147,7 +153,7 @@ size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
 /* Routing of T tokens, entirely on the device, no host synchronisation:
    router logits (unless MOE_LOGITS_IN), top-k selection and renormalised
    scores, histogram, exclusive scan, stable scatter into expert-sorted order,
-   and both block maps.  x: bf16 [T][d].  ([Lily-M5] "Prefill: keep routing on
+   and both block maps (four kernels).  x: bf16 [T][d].  ([Lily-M5] "Prefill: keep routing on
    the GPU, dequantize in flight".) */
 int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
               const moe_routing* r, void* stream);
@@ -179,7 +185,8 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
 /* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill and
    moe_decode call made on this host thread records events[0] on its stream
    before its first kernel and events[i] right after its i-th kernel, for
-   i < n (moe_route: router logits, top-k, sort; moe_prefill: gate/up, down
+   i < n (moe_route: router logits, top-k, histogram, scan + scatter + maps;
+   moe_prefill: gate/up, down
    (routed and shared), combine; moe_decode: router partial sums, router sum +
    top-k, gate/up, down).  With MOE_LOGITS_IN the router-logit slot is still
    recorded but brackets no kernel.  The

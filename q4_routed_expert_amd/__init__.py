@@ -101,6 +101,8 @@ class DeviceRouting:
         self.n_blocks = torch.zeros(1, **i32)
         self.tile_map = torch.zeros((nt, 2), **i32)
         self.n_tiles = torch.zeros(1, **i32)
+        n_blk = (T + _abi.MOE_ROUTE_BLOCK - 1) // _abi.MOE_ROUTE_BLOCK
+        self.blk_counts = torch.zeros((n_blk, n_experts), **i32)
         self.struct = _abi.Routing(*[_ptr(getattr(self, f)) for f, _ in _abi.Routing._fields_])
 
 

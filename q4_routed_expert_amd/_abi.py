@@ -10,6 +10,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 MOE_LOGITS_IN = 1
 MOE_BLOCK_ROWS = 32
 MOE_TILE_ROWS = 128
+MOE_ROUTE_BLOCK = 256
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_D, MOE_MAX_INTER = 256, 8, 32768, 8192, 2048
 
 # every function include/q4moe.h declares
@@ -31,7 +32,7 @@ class Layer(C.Structure):
 class Routing(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("logits", "topk_idx", "topk_w", "counts", "offsets",
                                           "perm", "inv_perm", "block_map", "n_blocks",
-                                          "tile_map", "n_tiles")]
+                                          "tile_map", "n_tiles", "blk_counts")]
 
 
 _lib = None

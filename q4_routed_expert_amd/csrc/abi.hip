@@ -88,7 +88,8 @@ int check_routing(const moe_routing* r) {
         (rc = check_ptr(r->block_map, "routing.block_map")) ||
         (rc = check_ptr(r->n_blocks, "routing.n_blocks")) ||
         (rc = check_ptr(r->tile_map, "routing.tile_map")) ||
-        (rc = check_ptr(r->n_tiles, "routing.n_tiles")))
+        (rc = check_ptr(r->n_tiles, "routing.n_tiles")) ||
+        (rc = check_ptr(r->blk_counts, "routing.blk_counts")))
         return rc;
     return MOE_OK;
 }

@@ -9,6 +9,7 @@ namespace q4moe {
 
 static_assert(kMaxExperts == MOE_MAX_EXPERTS && kMaxTopK == MOE_MAX_TOPK, "limits");
 static_assert(kBlockRows == MOE_BLOCK_ROWS && kTileRows == MOE_TILE_ROWS, "map rows");
+static_assert(MOE_ROUTE_BLOCK == 256, "the routing kernels use one thread per token of a block");
 
 // Records the next event of the caller's timing hook (moe_trace_events) on s,
 // if one is installed on this host thread; called after every kernel launch.

@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
         const unsigned char* tile = lds + buf * kTileBytes;
         // chunks (or second halves) past K contribute zero weights
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-        const float s0 = ok0 ? bf16_to_f32(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
-        const float s1 = ok1 ? bf16_to_f32(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
+        const float s0 = ok0 ? dq_scale(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
+        const float s1 = ok1 ? dq_scale(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
         const int arow = lane & 31;
         bf16x8 Acur[NMS], Anxt[NMS];
 #pragma unroll
@@ -390,8 +390,8 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     auto compute = [&](auto nms_tag, int c, const BChunk& st) {
         constexpr int NMS = decltype(nms_tag)::value;
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-        const float s0 = ok0 ? bf16_to_f32(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
-        const float s1 = ok1 ? bf16_to_f32(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
+        const float s0 = ok0 ? dq_scale(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
+        const float s1 = ok1 ? dq_scale(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
         const int arow = lane & 31, sbase = c * kSlots;
         auto aread = [&](int ms, int slot) {
             const int row = 32 * ms + arow;
@@ -597,9 +597,9 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, 
             constexpr int NMS = decltype(nms_tag)::value;
             const unsigned char* tile = lds + buf * kTileBytes;
             const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-            const float s0 = ok0 ? bf16_to_f32(st.sp & 0xFFFFu) : 0.0f;
+            const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f;
             const float b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
-            const float s1 = ok1 ? bf16_to_f32(st.sp >> 16) : 0.0f;
+            const float s1 = ok1 ? dq_scale(st.sp >> 16) : 0.0f;
             const float b1 = ok1 ? bf16_to_f32(st.bp >> 16) : 0.0f;
             // row 32*ms + lane%32 has (row & 15) == (lane & 15) for every ms, so the
             // swizzled slot offset is shared by the subtiles
@@ -792,7 +792,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(Q4 m, int n_rows, int K,
     if (i >= words) return;
     const size_t n = i / (K / 8), kw = i % (K / 8);
     const size_t g = n * (K / kGroup) + (kw * 8) / kGroup;
-    const bf16x8 v = dequant8(m.q[i], bf16_to_f32(m.scale[g]), bf16_to_f32(m.bias[g]));
+    const bf16x8 v = dequant8(m.q[i], dq_scale(m.scale[g]), bf16_to_f32(m.bias[g]));
     *(bf16x8*)(w_out + n * K + kw * 8) = v;
 }
 

@@ -135,44 +135,50 @@ __device__ __forceinline__ float silu(float g) {
     return __fdividef(g, 1.0f + __expf(-g));
 }
 
-// Ordering key for "larger logit first, equal logits -> lower expert index":
-// a larger key wins.  -0.0 is folded onto +0.0 so that the two tie.
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+// Order-preserving 32-bit key of an fp32 logit: a larger logit has a larger
+// key.  -0.0 is folded onto +0.0 so that the two tie; key 0 belongs to no
+// finite logit.
+__device__ __forceinline__ uint32_t logit_key(float v) {
     if (v == 0.0f) v = 0.0f;
-    uint32_t u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xFFFFu - (uint32_t)e);
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int topk_key_expert(uint64_t key) {
-    return (int)(0xFFFFu - (uint32_t)(key & 0xFFFFu));
+__device__ __forceinline__ float key_logit(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-        uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
-    }
-    return v;
+// Maximum of v over the wave, returned to every lane: four DPP steps give
+// every lane the maximum of its row of 16 lanes (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16), then the four row maxima meet in
+// scalar registers.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false)); // row_mirror
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 // ---------------------------------------------------------------------------
-// Top-k of one token's logits by one wave (E <= 256: four logits per lane).
-// Selection compares fp32 logits: larger first, equal -> lower expert index.
+// Top-k of one token's logits by one wave (E <= 256: lane l holds experts
+// l, l + 64, l + 128, l + 192).  Selection compares fp32 logits: larger
+// first, equal logits -> lower expert index.  Each of the k rounds takes the
+// wave maximum of the keys, finds the lowest expert holding it from four
+// ballots (scalar work) and retires that key.
 // Scores: softmax over the experts renormalised over the k selected ones,
 // computed as exp(l_s - l_max) / sum_s' exp(l_s' - l_max) (the full-softmax
 // normaliser cancels).  Lane s < k returns slot s.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, int lane,
                                           int* out_e, float* out_w) {
-    uint64_t key[4];
+    uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? topk_key(lrow[e], e) : 0ull;
+        key[i] = e < E ? logit_key(lrow[e]) : 0u;
     }
     float sel_l[kMaxTopK];
     int sel_e[kMaxTopK];
@@ -181,18 +187,22 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E,
         sel_l[s] = 0.0f;
         sel_e[s] = 0;
         if (s < k) {
-            uint64_t b = key[0];
-#pragma unroll
-            for (int i = 1; i < 4; ++i) b = key[i] > b ? key[i] : b;
-            b = wave_max_u64(b);
-            const int e = topk_key_expert(b);
+            const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+            const uint64_t b0 = __builtin_amdgcn_ballot_w64(key[0] == m);
+            const uint64_t b1 = __builtin_amdgcn_ballot_w64(key[1] == m);
+            const uint64_t b2 = __builtin_amdgcn_ballot_w64(key[2] == m);
+            const uint64_t b3 = __builtin_amdgcn_ballot_w64(key[3] == m);
+            const int e = b0 ? __builtin_ctzll(b0)
+                        : b1 ? 64 + __builtin_ctzll(b1)
+                        : b2 ? 128 + __builtin_ctzll(b2)
+                             : 192 + __builtin_ctzll(b3);
             if ((e & 63) == lane) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (i == (e >> 6)) key[i] = 0ull;
+                    if (i == (e >> 6)) key[i] = 0u;
             }
             sel_e[s] = e;
-            sel_l[s] = lrow[e];
+            sel_l[s] = key_logit(m);
         }
     }
     float ex[kMaxTopK], sum = 0.0f;

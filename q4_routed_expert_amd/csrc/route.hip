@@ -1,7 +1,7 @@
 // route.hip -- GPU-resident routing of one chunk of T tokens:
 //   router logits -> top-k + renormalised scores -> histogram -> exclusive scan
 //   -> stable scatter into expert-sorted order -> 32-row block map and the
-//   128-row work map of the grouped GEMMs.
+//   128-row work map of the grouped GEMMs (four kernels).
 // All of it stays on the device in one stream with no host synchronisation
 // ([Lily-M5] "Prefill: keep routing on the GPU, dequantize in flight": grouped
 // GEMM needs each expert's rows stored together, hence histogram, prefix scan,
@@ -132,55 +132,68 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
 }
 
 // ---------------------------------------------------------------------------
-// Histogram, exclusive scan, stable scatter and block maps in one work group
-// of 16 waves.  Wave w owns a contiguous token range (so ranges are in token
-// order across waves).
-//   1. per-wave per-expert totals with LDS atomic adds (order independent);
-//   2. counts = column sums; each wave's base = exclusive sum over lower waves;
-//   3. one wave scans counts, ceil(counts/32) and ceil(counts/128) over the
-//      experts: offsets and the starts of each expert's tiles in both maps;
-//   4. the maps: (expert, first sorted row) per tile, experts ascending;
-//   5. stable scatter: per 64-token chunk each lane ORs its bit into a 64-bit
-//      mask per expert; a lane's rank among the chunk's rows of expert e is
-//      popcount(mask[e] & lanes-below), so sorted row = offsets[e] +
-//      wave base[e] + rows of e in the wave's earlier chunks + rank.
-// Every step is deterministic, so perm is the same on every run and equals
-// the sequential stable order (token ascending inside each expert).
+// Histogram, exclusive scan, stable scatter and block maps, in two kernels
+// over blocks of kRouteBlock consecutive tokens.
+//   route_count_kernel (one work group per block): the block's per-expert
+//     assignment counts, with LDS atomic adds (integer, so order does not
+//     matter), written to blk_counts[block][E];
+//   route_scatter_kernel (one work group per block):
+//     1. per expert: the total count and the count of the earlier blocks
+//        (a fixed-order sum over the count table);
+//     2. one wave scans the totals, ceil(totals/32) and ceil(totals/128) over
+//        the experts: offsets and the first entry of each expert's tiles in
+//        both maps (block 0 writes counts, offsets and both maps);
+//     3. stable scatter: each wave owns 64 consecutive tokens; each lane ORs
+//        its bit into a 64-bit mask per expert, and the sorted row of
+//        (token, slot) is offsets[e] + rows of e in earlier blocks + rows of e
+//        in the block's earlier waves + popcount(mask[e] & lanes below).
+// Every step is deterministic and the result equals the sequential stable
+// order (token ascending inside each expert).
 // ---------------------------------------------------------------------------
-constexpr int kSortWaves = 16;
+constexpr int kRouteBlock = MOE_ROUTE_BLOCK;
+constexpr int kRouteWaves = kRouteBlock / 64;
+static_assert(kRouteBlock % 64 == 0 && kRouteBlock >= kMaxExperts, "route block");
 
-__global__ __launch_bounds__(1024) void route_sort_kernel(
-    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
-    int32_t* __restrict__ block_map, int32_t* __restrict__ n_blocks,
-    int32_t* __restrict__ tile_map, int32_t* __restrict__ n_tiles) {
-    __shared__ unsigned long long mask[kSortWaves][kMaxExperts];
-    __shared__ int run[kSortWaves][kMaxExperts];
-    __shared__ int s_cnt[kMaxExperts];
+__global__ __launch_bounds__(kRouteBlock) void route_count_kernel(const int32_t* __restrict__ idx,
+                                                                  int T, int k, int E,
+                                                                  int32_t* __restrict__ blk_counts) {
+    __shared__ int h[kMaxExperts];
+    const int tid = threadIdx.x, b = blockIdx.x;
+    if (tid < E) h[tid] = 0;
+    __syncthreads();
+    const int t = b * kRouteBlock + tid;
+    if (t < T)
+        for (int s = 0; s < k; ++s) atomicAdd(&h[idx[(size_t)t * k + s]], 1);
+    __syncthreads();
+    if (tid < E) blk_counts[(size_t)b * E + tid] = h[tid];
+}
+
+__global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ blk_counts,
+    int n_blk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm, int32_t* __restrict__ block_map,
+    int32_t* __restrict__ n_blocks, int32_t* __restrict__ tile_map, int32_t* __restrict__ n_tiles) {
+    __shared__ unsigned long long mask[kRouteWaves][kMaxExperts];
+    __shared__ int run[kRouteWaves][kMaxExperts];
+    __shared__ int s_cnt[kMaxExperts], s_before[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1], s_b32[kMaxExperts + 1], s_b128[kMaxExperts + 1];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_chunks = (T + 63) / 64;
-    const int cpw = (n_chunks + kSortWaves - 1) / kSortWaves;  // chunks per wave
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = blockIdx.x;
 
-    for (int i = tid; i < kSortWaves * kMaxExperts; i += 1024) (&run[0][0])[i] = 0;
-    __syncthreads();
-    for (int c = 0; c < cpw; ++c) {  // 1
-        const int t = (wave * cpw + c) * 64 + lane;
-        if (t < T)
-            for (int s = 0; s < k; ++s) atomicAdd(&run[wave][idx[(size_t)t * k + s]], 1);
-    }
-    __syncthreads();
-    if (tid < E) {  // 2
-        int acc = 0;
-        for (int w = 0; w < kSortWaves; ++w) {
-            const int v = run[w][tid];
-            run[w][tid] = acc;
-            acc += v;
+    // 1. totals and earlier-block counts
+    if (tid < E) {
+        int tot = 0, before = 0;
+        for (int b = 0; b < n_blk; ++b) {
+            const int c = blk_counts[(size_t)b * E + tid];
+            before += b < g ? c : 0;
+            tot += c;
         }
-        s_cnt[tid] = acc;
+        s_cnt[tid] = tot;
+        s_before[tid] = before;
     }
+    for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteBlock) (&mask[0][0])[i] = 0ull;
     __syncthreads();
-    if (wave == 0) {  // 3
+    // 2. scan over the experts (wave 0, four experts per lane)
+    if (wave == 0) {
         int c[4], b32[4], b128[4], sc = 0, s32 = 0, s128 = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -223,8 +236,20 @@ __global__ __launch_bounds__(1024) void route_sort_kernel(
             s_b128[E] = i128;
         }
     }
+    // 3a. this block's token masks
+    const int t = g * kRouteBlock + tid;
+    const bool valid = t < T;
+    int ex[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        ex[s] = 0;
+        if (valid && s < k) {
+            ex[s] = idx[(size_t)t * k + s];
+            atomicOr(&mask[wave][ex[s]], 1ull << lane);
+        }
+    }
     __syncthreads();
-    if (tid < E) {  // 4
+    if (g == 0 && tid < E) {  // 2b. counts, offsets and both maps
         const int c = s_cnt[tid], o = s_off[tid];
         counts[tid] = c;
         offsets[tid] = o;
@@ -238,48 +263,45 @@ __global__ __launch_bounds__(1024) void route_sort_kernel(
             tile_map[2 * b] = tid;
             tile_map[2 * b + 1] = o + kTileRows * j;
         }
-    }
-    if (tid == 0) {
-        offsets[E] = s_off[E];
-        *n_blocks = s_b32[E];
-        *n_tiles = s_b128[E];
-    }
-    for (int c = 0; c < cpw; ++c) {  // 5
-        for (int i = lane; i < kMaxExperts; i += 64) mask[wave][i] = 0ull;
-        __syncthreads();
-        const int t = (wave * cpw + c) * 64 + lane;
-        const bool valid = t < T;
-        int ex[kMaxTopK];
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            ex[s] = 0;
-            if (valid && s < k) {
-                ex[s] = idx[(size_t)t * k + s];
-                atomicOr(&mask[wave][ex[s]], 1ull << lane);
-            }
+        if (tid == 0) {
+            offsets[E] = s_off[E];
+            *n_blocks = s_b32[E];
+            *n_tiles = s_b128[E];
         }
-        __syncthreads();
-        const unsigned long long below = (1ull << lane) - 1ull;
+    }
+    if (tid < E) {  // rows of each expert in the block's earlier waves
+        int acc = 0;
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (valid && s < k) {
-                const int e = ex[s];
-                const int pos = s_off[e] + run[wave][e] + __popcll(mask[wave][e] & below);
-                perm[pos] = t * k + s;
-                inv_perm[(size_t)t * k + s] = pos;
-            }
+        for (int w = 0; w < kRouteWaves; ++w) {
+            run[w][tid] = acc;
+            acc += __popcll(mask[w][tid]);
         }
-        __syncthreads();
-        for (int i = lane; i < E; i += 64) run[wave][i] += __popcll(mask[wave][i]);
-        __syncthreads();
+    }
+    __syncthreads();
+    // 3b. scatter
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (valid && s < k) {
+            const int e = ex[s];
+            const int pos = s_off[e] + s_before[e] + run[wave][e] + __popcll(mask[wave][e] & below);
+            perm[pos] = t * k + s;
+            inv_perm[(size_t)t * k + s] = pos;
+        }
     }
 }
 
 hipError_t launch_route_sort(const int32_t* idx, int T, int k, int E, const moe_routing* r,
                              hipStream_t s) {
-    hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(1024), 0, s, idx, T, k, E, r->counts,
-                       r->offsets, r->perm, r->inv_perm, r->block_map, r->n_blocks, r->tile_map,
-                       r->n_tiles);
+    const int n_blk = (T + kRouteBlock - 1) / kRouteBlock;
+    hipLaunchKernelGGL(route_count_kernel, dim3(n_blk), dim3(kRouteBlock), 0, s, idx, T, k, E,
+                       r->blk_counts);
+    trace_point(s);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(n_blk), dim3(kRouteBlock), 0, s, idx, T, k, E,
+                       r->blk_counts, n_blk, r->counts, r->offsets, r->perm, r->inv_perm,
+                       r->block_map, r->n_blocks, r->tile_map, r->n_tiles);
     trace_point(s);
     return hipGetLastError();
 }
