@@ -441,8 +441,9 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
 }
 
 // ---------------------------------------------------------------------------
-// Persistent gate/up GEMM.  One work group per CU walks a static list of
-// units (work item, 128-intermediate-column block): unit u = g, g + G, ...
+// Persistent gate/up GEMM.  One work group of eight waves per CU walks a
+// static list of units (work item, 128-intermediate-column block):
+// unit u = g, g + G, ...
 // where G is the grid size.  Units are numbered so that the column blocks of
 // one item have the same index modulo 8 and therefore run on one XCD (work
 // groups are dispatched to the 8 XCDs round-robin), sharing its L2 for the
@@ -457,11 +458,16 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
 // (lanes 16-31).  In the 32x32 output tile a lane then holds gate row r and
 // up row r + 16 of the same token in elements i and i + 8, so SiLU(gate)*up
 // needs no data exchange.
-// Weights stream three chunks ahead and activations two (activations of the
-// chunk two ahead are issued before the weights of the chunk three ahead, so
-// waiting for an activation chunk never waits for younger weight loads).
+// Weights stream two chunks ahead and activations one (activations are
+// issued before the weights, so waiting for an activation chunk never waits
+// for younger weight loads).
 // ---------------------------------------------------------------------------
 constexpr int kBatch = 8;
+constexpr int kGuWaves = 8;
+constexpr int kGuThreads = kGuWaves * 64;
+constexpr int kGuCols = 16 * kGuWaves;                // intermediate columns per unit
+constexpr int kGuALoads = kMT * kSlots / kGuThreads;  // 16-byte activation loads per lane per chunk
+static_assert(kMT * kSlots % kGuThreads == 0, "activation tile split");
 
 struct UnitDesc {
     int e, row0, M, cb, shared;
@@ -486,7 +492,7 @@ struct WChunk {
     uint32_t sp, bp;
 };
 
-__global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, const int n_cb) {
+__global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a, const int n_cb) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
     __shared__ UnitDesc s_unit[kBatch];
     __shared__ int s_src[kBatch][kMT];
@@ -506,7 +512,11 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, 
 
     f32x16 acc[4];
     WChunk bst[kStages];
-    u32x4 ast[kStages][kALoads];
+    u32x4 ast[kGuALoads];                      // the activation chunk after the current one
+    uint32_t a_row[kGuALoads];                 // activation stream: row offsets of its unit
+    const uint32_t* w_q = nullptr;             // weight stream: this lane's row in its unit
+    const uint16_t* w_s = nullptr;
+    const uint16_t* w_b = nullptr;
 
     int u_next = g;
     while (true) {
@@ -542,54 +552,67 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, 
         }
         if (nb == 0) break;
         __syncthreads();
+        int a_unit = -1, w_unit = -1;
 
         // ---- loaders (clamped to valid addresses, never under a branch) ----
         // Rows past M were given source row 0 in the descriptor (their products
-        // are never stored), and columns at or past K read column 0 of the row
-        // (their weights are zeroed in compute), so every load stays inside x.
-        // The column slot is the same for the kALoads loads of a lane.
-        auto load_a = [&](int sp, u32x4 (&areg)[kALoads]) {
+        // are never stored), and columns at or past K read a column of the same
+        // row below 64 (their weights are zeroed in compute), so every load
+        // stays inside x.  The activation and weight streams each keep the
+        // per-lane addresses of the unit they are reading in registers and
+        // refresh them from LDS only when they cross into the next unit, so
+        // the per-chunk work is a few adds.
+        auto load_a = [&](int sp, u32x4 (&areg)[kGuALoads]) {
             sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
             const int bb = sp / NL, c = sp - bb * NL;
-            const int kc = c * kKC + 8 * (tid & 15);
-            const uint32_t col = kc < K ? (uint32_t)kc : 0u;
+            if (bb != a_unit) {  // uniform: once per unit
+                a_unit = bb;
 #pragma unroll
-            for (int p = 0; p < kALoads; ++p) {
-                const int row = (tid + kThreads * p) >> 4;
-                const uint32_t off = (uint32_t)s_src[bb][row] * (uint32_t)K + col;
-                areg[p] = *(const u32x4*)(a.x + off);
+                for (int p = 0; p < kGuALoads; ++p)
+                    a_row[p] = (uint32_t)s_src[bb][(tid + kGuThreads * p) >> 4] * (uint32_t)K;
             }
+            const int kc = c * kKC + 8 * (tid & 15);
+            const uint32_t col = kc < K ? (uint32_t)kc : (uint32_t)(kc & 63);
+#pragma unroll
+            for (int p = 0; p < kGuALoads; ++p) areg[p] = *(const u32x4*)(a.x + (a_row[p] + col));
         };
         auto load_b = [&](int sp, WChunk& st) {
             sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
             const int bb = sp / NL, c = sp - bb * NL;
-            const UnitDesc ud = uniform_desc(s_unit[bb]);
-            const Q4 Wg = ud.shared ? a.sh_gate : a.gate;
-            const Q4 Wu = ud.shared ? a.sh_up : a.up;
-            const int j0 = ud.cb * 128 + 16 * wave;
-            const size_t wrow = (size_t)ud.e * Nw + (j0 < Nw ? j0 + jrow : 0);
-            const uint32_t* qb = is_up ? Wu.q : Wg.q;
-            const uint16_t* sb = is_up ? Wu.scale : Wg.scale;
-            const uint16_t* bbp = is_up ? Wu.bias : Wg.bias;
+            if (bb != w_unit) {  // uniform: once per unit
+                w_unit = bb;
+                const UnitDesc ud = uniform_desc(s_unit[bb]);
+                // field by field: selecting a whole Q4 by a per-lane condition
+                // would read it from the kernel arguments through memory
+                const bool sh = ud.shared != 0;
+                const uint32_t* gq = sh ? a.sh_gate.q : a.gate.q;
+                const uint32_t* uq = sh ? a.sh_up.q : a.up.q;
+                const uint16_t* gs = sh ? a.sh_gate.scale : a.gate.scale;
+                const uint16_t* us = sh ? a.sh_up.scale : a.up.scale;
+                const uint16_t* gb = sh ? a.sh_gate.bias : a.gate.bias;
+                const uint16_t* ub = sh ? a.sh_up.bias : a.up.bias;
+                const int j0 = ud.cb * kGuCols + 16 * wave;
+                const size_t wrow = (size_t)ud.e * Nw + (j0 < Nw ? j0 + jrow : 0);
+                w_q = (is_up ? uq : gq) + wrow * (K / 8) + 4 * half;
+                w_s = (is_up ? us : gs) + wrow * (K / kGroup);
+                w_b = (is_up ? ub : gb) + wrow * (K / kGroup);
+            }
             const int kc0 = c * kKC < K ? c * kKC : 0;
             const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
-            const uint32_t* qrow = qb + wrow * (K / 8) + 4 * half;
-            const size_t gi = wrow * (K / kGroup) + kc0 / kGroup;
-            st.lo = *(const u32x4*)(qrow + kc0 / 8);
-            st.hi = *(const u32x4*)(qrow + kc1 / 8);
+            st.lo = *(const u32x4*)(w_q + kc0 / 8);
+            st.hi = *(const u32x4*)(w_q + kc1 / 8);
             if (pair_sb) {
-                st.sp = *(const uint32_t*)(sb + gi);
-                st.bp = *(const uint32_t*)(bbp + gi);
+                st.sp = *(const uint32_t*)(w_s + kc0 / kGroup);
+                st.bp = *(const uint32_t*)(w_b + kc0 / kGroup);
             } else {  // odd group count: two 2-byte loads each
-                const size_t g1 = wrow * (K / kGroup) + kc1 / kGroup;
-                st.sp = (uint32_t)sb[gi] | ((uint32_t)sb[g1] << 16);
-                st.bp = (uint32_t)bbp[gi] | ((uint32_t)bbp[g1] << 16);
+                st.sp = (uint32_t)w_s[kc0 / kGroup] | ((uint32_t)w_s[kc1 / kGroup] << 16);
+                st.bp = (uint32_t)w_b[kc0 / kGroup] | ((uint32_t)w_b[kc1 / kGroup] << 16);
             }
         };
-        auto store_a = [&](int buf, const u32x4 (&areg)[kALoads]) {
+        auto store_a = [&](int buf, const u32x4 (&areg)[kGuALoads]) {
 #pragma unroll
-            for (int p = 0; p < kALoads; ++p) {
-                const int i = tid + kThreads * p, row = i >> 4, slot = i & 15;
+            for (int p = 0; p < kGuALoads; ++p) {
+                const int i = tid + kGuThreads * p, row = i >> 4, slot = i & 15;
                 *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = areg[p];
             }
         };
@@ -634,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, 
         auto epilogue = [&](int bb) {
             const UnitDesc ud = uniform_desc(s_unit[bb]);
             const int n_ms = (ud.M + 31) >> 5;
-            const int j0 = ud.cb * 128 + 16 * wave;
+            const int j0 = ud.cb * kGuCols + 16 * wave;
             if (j0 < Nw) {
                 uint16_t* out = ud.shared ? a.h_sh : a.h;
 #pragma unroll
@@ -660,15 +683,18 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, 
         };
         auto unit_loop = [&](auto nms_tag, int bb) {
             const int cbu = __builtin_amdgcn_readfirstlane(s_unit[bb].cb);
-            const bool on = cbu * 128 + 16 * wave < Nw;
+            const bool on = cbu * kGuCols + 16 * wave < Nw;
             for (int c0 = 0; c0 < NL; c0 += kStages) {
 #pragma unroll
                 for (int u = 0; u < kStages; ++u) {
                     const int c = c0 + u, sp = bb * NL + c;
-                    store_a(u & 1, ast[u]);
+                    store_a(u & 1, ast);
                     __syncthreads();
-                    load_a(sp + 2, ast[(u + 2) % kStages]);
-                    load_b(sp + 3, bst[(u + 3) % kStages]);
+                    load_a(sp + 1, ast);  // chunk c+1 reuses the registers of chunk c
+                    // keep the activation loads older than the weight loads: the
+                    // next chunk's stores then wait for activations only
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_b(sp + 2, bst[(u + 2) % kStages]);
                     if (on) compute(nms_tag, c, u & 1, bst[u]);
                 }
             }
@@ -677,10 +703,9 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(const PrefillArgs a, 
         // ---- the batch: one continuous pipeline over nb units ----
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
-        load_a(0, ast[0]);
-        load_a(1, ast[1]);
-#pragma unroll
-        for (int u = 0; u < kStages - 1; ++u) load_b(u, bst[u]);
+        load_a(0, ast);
+        load_b(0, bst[0]);
+        load_b(1, bst[1]);
         for (int bb = 0; bb < nb; ++bb) {
             switch ((__builtin_amdgcn_readfirstlane(s_unit[bb].M) + 31) >> 5) {
                 case 1: unit_loop(Int<1>{}, bb); break;
@@ -708,12 +733,12 @@ static int device_cus() {
 }
 
 static hipError_t launch_gate_up(const PrefillArgs& a, hipStream_t s) {
-    const int n_cb = (a.I + 127) / 128;
+    const int n_cb = (a.I + kGuCols - 1) / kGuCols;
     const int sh_items = (a.T + kMT - 1) / kMT;
     const int max_units = (a.tile_bound + sh_items + 7) / 8 * 8 * n_cb;
     int grid = device_cus();
     if (grid > max_units) grid = max_units;
-    hipLaunchKernelGGL(gate_up_kernel, dim3(grid), dim3(kThreads), 0, s, a, n_cb);
+    hipLaunchKernelGGL(gate_up_kernel, dim3(grid), dim3(kGuThreads), 0, s, a, n_cb);
     trace_point(s);
     return hipGetLastError();
 }
