@@ -211,7 +211,7 @@ def bench_decode(args, q4, torch, ev, stream):
     torch.cuda.synchronize()
     calls = n_steps * n_layers
     us_layer = ev.ms(t[0], t[1]) * 1e3 / calls
-    names = ["router_partial", "router_topk", "gate_up", "down"]
+    names = ["router_partial", "router_topk", "gate_up", "down_combine"]
     per = {n: sum(ev.ms(ev_d[li][j], ev_d[li][j + 1]) for li in range(n_layers)) * 1e3 / n_layers
            for j, n in enumerate(names)}
     expert_bytes = (w.top_k + 1) * (2 * q4_bytes(w.inter, w.d) + q4_bytes(w.d, w.inter))
@@ -255,7 +255,7 @@ def bench_decode(args, q4, torch, ev, stream):
     out["roofline"] = {"bound": "hbm", "achieved": round(ex_bytes / k_sec / 1e9, 1),
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                        "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
-                       "kernels": "decode router partial + router top-k + gate/up + down"}
+                       "kernels": "decode router partial + router top-k + gate/up + down/combine"}
     del layers, ws
     torch.cuda.empty_cache()
     return out

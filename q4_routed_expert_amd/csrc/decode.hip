@@ -7,16 +7,18 @@
 // projections fused with the gate activation, the output projection fused
 // with the routing scores and the shared expert, intermediates in registers.
 //
-// Four launches on one stream:
-//   1. router partial sums: d/32 work groups each sum 32 rows of x . W_r for
-//      every expert (skipped when the logits are given);
-//   2. one work group adds the partial sums in a fixed order, applies the
-//      bias and runs the top-k;
-//   3. gate/up: one wave per (selected or shared expert, 4 intermediate rows);
-//      the gate and up rows are streamed once with 16-byte loads and
+// Four launches on one stream, each spread over thousands of waves so that
+// the weight loads of many waves are in flight at once:
+//   1. router partial sums: d/32 work groups, each sums 32 rows of x . W_r
+//      for every expert (skipped when the logits are given);
+//   2. one work group adds the partial sums in a fixed order (four quarters
+//      in parallel, then the quarters in order), applies the bias and runs
+//      the top-k;
+//   3. gate/up: one wave per (selected or shared expert, intermediate row j):
+//      the gate and up rows are streamed once with 16-byte loads per lane and
 //      h = bf16(SiLU(g) * u) is written;
-//   4. down: each wave produces 4 outputs; for each it streams the row of all
-//      k + 1 experts' down matrices and combines
+//   4. down: one wave per output n: each lane takes one code word of each of
+//      the k + 1 experts' rows, and the wave combines
 //      y = bf16( sum_s w_s * P_s (slot order) + P_shared ).
 // Every weight enters as the bf16 value bf16(q * s + b), the same operand the
 // grouped GEMM feeds its matrix cores, so prefill and decode compute one
@@ -25,9 +27,10 @@
 
 namespace q4moe {
 
-constexpr int kRouterRows = 32;  // rows of W_r per router work group
-constexpr int kGuRows = 4;       // gate/up rows per wave
-constexpr int kDnRows = 4;       // down outputs per wave
+constexpr int kRouterRows = 32;  // rows of W_r per router work group (DecodeWs sizes partial by it)
+constexpr int kRouterQuarters = 4;
+
+static_assert(kRouterRows == MOE_DECODE_ROUTER_ROWS, "router partial rows");
 
 // Partial router sums over 32 rows of W_r: partial[g][e] = sum_j x[32g+j] W_r[32g+j][e].
 __global__ __launch_bounds__(256) void decode_router_partial_kernel(const DecodeArgs a) {
@@ -44,24 +47,38 @@ __global__ __launch_bounds__(256) void decode_router_partial_kernel(const Decode
     a.partial[(size_t)g * E + e] = acc;
 }
 
-// Logits = partial sums added in a fixed order (+ bias), then top-k by one wave.
-__global__ __launch_bounds__(256) void decode_router_topk_kernel(const DecodeArgs a, int n_part) {
+// Logits = partial sums added in a fixed order (+ bias), then top-k by one
+// wave.  Thread (q, e) sums the q-th quarter of expert e's partials, 16 loads
+// in flight at a time (one batch for d = 2048); the quarters are then added
+// in order.
+__global__ __launch_bounds__(1024) void decode_router_topk_kernel(const DecodeArgs a, int n_part) {
+    __shared__ float s_q[kRouterQuarters][kMaxExperts];
     __shared__ float s_logits[kMaxExperts];
     const int tid = threadIdx.x, E = a.E;
+    const int e = tid & (kMaxExperts - 1), q = tid / kMaxExperts;
+    if (!a.logits_in && e < E) {
+        const int per = (n_part + kRouterQuarters - 1) / kRouterQuarters;
+        const int g_beg = q * per, g_end = min(n_part, g_beg + per);
+        float v = 0.0f;
+        for (int g0 = g_beg; g0 < g_end; g0 += 16) {
+            float p[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int gg = g0 + u < g_end ? g0 + u : g_beg;  // clamped, always valid
+                p[u] = a.partial[(size_t)gg * E + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v += g0 + u < g_end ? p[u] : 0.0f;
+        }
+        s_q[q][e] = v;
+    }
+    __syncthreads();
     if (tid < E) {
         float v;
         if (a.logits_in) {
             v = a.logits[tid];
         } else {
-            float p[8];
-            v = 0.0f;
-            for (int g0 = 0; g0 < n_part; g0 += 8) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    p[u] = g0 + u < n_part ? a.partial[(size_t)(g0 + u) * E + tid] : 0.0f;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v += p[u];
-            }
+            v = ((s_q[0][tid] + s_q[1][tid]) + s_q[2][tid]) + s_q[3][tid];
             if (a.router_bias) v += a.router_bias[tid];
             a.logits[tid] = v;
         }
@@ -69,127 +86,104 @@ __global__ __launch_bounds__(256) void decode_router_topk_kernel(const DecodeArg
     }
     __syncthreads();
     if (tid < 64) {
-        int e;
-        float w;
-        wave_topk(s_logits, E, a.k, tid, &e, &w);
+        int se;
+        float sw;
+        wave_topk(s_logits, E, a.k, tid, &se, &sw);
         if (tid < a.k) {
-            a.sel_idx[tid] = e;
-            a.sel_w[tid] = w;
-            if (a.out_idx) a.out_idx[tid] = e;
-            if (a.out_w) a.out_w[tid] = w;
+            a.sel_idx[tid] = se;
+            a.sel_w[tid] = sw;
+            if (a.out_idx) a.out_idx[tid] = se;
+            if (a.out_w) a.out_w[tid] = sw;
         }
     }
 }
 
-// One wave per (slot, 4 intermediate rows j); lane covers 32 consecutive k
-// of each 2048-wide pass (half a quantisation group).  All of the wave's
-// loads are issued before any arithmetic.  Weights are the bf16 values
-// bf16(q * s + b), as in the grouped GEMM, dotted with bf16 x in fp32.
+// One wave per (slot, intermediate row j); lane covers 32 consecutive k of
+// each 2048-wide pass (half a quantisation group).  Weights are the bf16
+// values bf16(q * s + b), as in the grouped GEMM, dotted with bf16 x in fp32.
 __global__ __launch_bounds__(256) void decode_gate_up_kernel(const DecodeArgs a) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int slot = blockIdx.y;  // 0..k-1 routed, k = shared
-    const int j0 = (blockIdx.x * 4 + wave) * kGuRows;
-    if (j0 >= a.I) return;
+    if (j >= a.I) return;
     const int d = a.d;
-    Q4 G, U;
-    size_t row0;
-    if (slot < a.k) {
-        row0 = (size_t)a.sel_idx[slot] * a.I + j0;
-        G = a.gate;
-        U = a.up;
-    } else {
-        row0 = j0;
-        G = a.sh_gate;
-        U = a.sh_up;
-    }
-    float gsum[kGuRows] = {}, usum[kGuRows] = {};
+    const bool shared = slot >= a.k;
+    const size_t row = shared ? (size_t)j : (size_t)a.sel_idx[slot] * a.I + j;
+    const uint32_t* gq = (shared ? a.sh_gate.q : a.gate.q) + row * (d / 8);
+    const uint32_t* uq = (shared ? a.sh_up.q : a.up.q) + row * (d / 8);
+    const uint16_t* gs = (shared ? a.sh_gate.scale : a.gate.scale) + row * (d / kGroup);
+    const uint16_t* gb = (shared ? a.sh_gate.bias : a.gate.bias) + row * (d / kGroup);
+    const uint16_t* us = (shared ? a.sh_up.scale : a.up.scale) + row * (d / kGroup);
+    const uint16_t* ub = (shared ? a.sh_up.bias : a.up.bias) + row * (d / kGroup);
+    float gsum = 0.0f, usum = 0.0f;
     for (int kb = 0; kb < d; kb += 64 * 32) {
         const int k0 = kb + 32 * lane;
-        if (k0 < d) {
-            u32x4 gq[kGuRows], uq[kGuRows], xv[4];
-            float gs[kGuRows], gb[kGuRows], us[kGuRows], ub[kGuRows];
+        const int kk = k0 < d ? k0 : 0;  // clamped, always valid; masked below
+        const u32x4 gw = *(const u32x4*)(gq + kk / 8);
+        const u32x4 uw = *(const u32x4*)(uq + kk / 8);
+        const float g_s = dq_scale(gs[kk / kGroup]), g_b = bf16_to_f32(gb[kk / kGroup]);
+        const float u_s = dq_scale(us[kk / kGroup]), u_b = bf16_to_f32(ub[kk / kGroup]);
+        u32x4 xv[4];
 #pragma unroll
-            for (int r = 0; r < kGuRows; ++r) {
-                const size_t row = row0 + r;
-                gq[r] = *(const u32x4*)(G.q + row * (d / 8) + k0 / 8);
-                uq[r] = *(const u32x4*)(U.q + row * (d / 8) + k0 / 8);
-                const size_t gi = row * (d / kGroup) + k0 / kGroup;
-                gs[r] = dq_scale(G.scale[gi]);
-                gb[r] = bf16_to_f32(G.bias[gi]);
-                us[r] = dq_scale(U.scale[gi]);
-                ub[r] = bf16_to_f32(U.bias[gi]);
-            }
+        for (int p = 0; p < 4; ++p) xv[p] = ((const u32x4*)(a.x + kk))[p];
+        float gp = 0.0f, up = 0.0f;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) xv[p] = ((const u32x4*)(a.x + k0))[p];
-#pragma unroll
-            for (int r = 0; r < kGuRows; ++r)
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    gsum[r] = dot8_bf16(gq[r][p], gs[r], gb[r], xv[p], gsum[r]);
-                    usum[r] = dot8_bf16(uq[r][p], us[r], ub[r], xv[p], usum[r]);
-                }
+        for (int p = 0; p < 4; ++p) {
+            gp = dot8_bf16(gw[p], g_s, g_b, xv[p], gp);
+            up = dot8_bf16(uw[p], u_s, u_b, xv[p], up);
         }
+        gsum += k0 < d ? gp : 0.0f;
+        usum += k0 < d ? up : 0.0f;
     }
-#pragma unroll
-    for (int r = 0; r < kGuRows; ++r) {
-        const float g = wave_sum(gsum[r]), u = wave_sum(usum[r]);
-        if (lane == r) a.h[(size_t)slot * a.I + j0 + r] = f32_to_bf16(silu(g) * u);
-    }
+    const float g = wave_sum_dpp(gsum), u = wave_sum_dpp(usum);
+    if (lane == 0) a.h[(size_t)slot * a.I + j] = f32_to_bf16(silu(g) * u);
 }
 
-// Each wave: 4 outputs n, 16 lanes per output, lane covers 32 consecutive k
-// of each 512-wide pass over the expert intermediate dimension.  The loads of
-// all k + 1 experts' rows are issued before the arithmetic; the combine then
-// adds w_s * P_s in slot order and the shared expert last.
+// One wave per output n; lane covers 8 consecutive intermediate k (one code
+// word) of each 512-wide pass, for every slot.  All slots' loads are issued
+// before the arithmetic; the combine then adds w_s * P_s in slot order and
+// the shared expert last.
 __global__ __launch_bounds__(256) void decode_down_kernel(const DecodeArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t s_h[];  // [(k+1)][I] bf16
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= a.d) return;
     const int I = a.I, k = a.k, d = a.d;
-    for (int i = tid; i < (k + 1) * I / 8; i += 256)
-        ((u32x4*)s_h)[i] = ((const u32x4*)a.h)[i];
-    __syncthreads();
-    const int n = (blockIdx.x * 4 + wave) * kDnRows + (lane >> 4);
-    const int c = lane & 15;
-    if (n >= d) return;
-    float part[kMaxTopK + 1] = {};
-    for (int kb = 0; kb < I; kb += 16 * 32) {
-        const int k0 = kb + 32 * c;
-        if (k0 >= I) continue;
-        u32x4 q[kMaxTopK + 1];
-        float sc[kMaxTopK + 1], bi[kMaxTopK + 1];
+    float part[kMaxTopK + 1];
+#pragma unroll
+    for (int s = 0; s <= kMaxTopK; ++s) part[s] = 0.0f;
+    for (int jb = 0; jb < I; jb += 64 * 8) {
+        const int j0 = jb + 8 * lane;
+        const int jj = j0 < I ? j0 : 0;  // clamped, always valid; masked below
+        uint32_t q[kMaxTopK + 1];
+        uint32_t sc[kMaxTopK + 1], bi[kMaxTopK + 1];
+        u32x4 hv[kMaxTopK + 1];
 #pragma unroll
         for (int s = 0; s <= kMaxTopK; ++s) {
-            q[s] = u32x4{0u, 0u, 0u, 0u};
-            sc[s] = bi[s] = 0.0f;
-            if (s <= k) {
-                const bool shared = s == k;
-                const Q4 D = shared ? a.sh_down : a.down;
-                const size_t row = shared ? (size_t)n : (size_t)a.sel_idx[s] * d + n;
-                q[s] = *(const u32x4*)(D.q + row * (I / 8) + k0 / 8);
-                const size_t gi = row * (I / kGroup) + k0 / kGroup;
-                sc[s] = dq_scale(D.scale[gi]);
-                bi[s] = bf16_to_f32(D.bias[gi]);
-            }
+            const int ss = s <= k ? s : k;  // slots past k repeat the shared expert (discarded)
+            const bool shared = ss == k;
+            const size_t row = shared ? (size_t)n : (size_t)a.sel_idx[ss] * d + n;
+            const Q4 D = shared ? a.sh_down : a.down;
+            q[s] = D.q[row * (I / 8) + jj / 8];
+            sc[s] = D.scale[row * (I / kGroup) + jj / kGroup];
+            bi[s] = D.bias[row * (I / kGroup) + jj / kGroup];
+            hv[s] = *(const u32x4*)(a.h + (size_t)ss * I + jj);
         }
 #pragma unroll
         for (int s = 0; s <= kMaxTopK; ++s) {
-            if (s <= k) {
-                const u32x4* hv = (const u32x4*)(s_h + (size_t)s * I + k0);
-#pragma unroll
-                for (int p = 0; p < 4; ++p) part[s] = dot8_bf16(q[s][p], sc[s], bi[s], hv[p], part[s]);
-            }
+            const float p = dot8_bf16(q[s], dq_scale(sc[s]), bf16_to_f32(bi[s]), hv[s], 0.0f);
+            part[s] += j0 < I ? p : 0.0f;
         }
     }
     float y = 0.0f, sh = 0.0f;
 #pragma unroll
     for (int s = 0; s <= kMaxTopK; ++s) {
         if (s <= k) {
-            const float p = group_sum<16>(part[s]);
+            const float p = wave_sum_dpp(part[s]);
             if (s < k) y += a.sel_w[s] * p;
             else sh = p;
         }
     }
-    if (c == 0) a.y[n] = f32_to_bf16(y + sh);
+    if (lane == 0) a.y[n] = f32_to_bf16(y + sh);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
@@ -197,26 +191,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (!a.logits_in)
         hipLaunchKernelGGL(decode_router_partial_kernel, dim3(n_part), dim3(256), 0, s, a);
     trace_point(s);
-    hipLaunchKernelGGL(decode_router_topk_kernel, dim3(1), dim3(256), 0, s, a, n_part);
+    hipLaunchKernelGGL(decode_router_topk_kernel, dim3(1), dim3(1024), 0, s, a, n_part);
     trace_point(s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int gu_waves = (a.I + kGuRows - 1) / kGuRows;
-    hipLaunchKernelGGL(decode_gate_up_kernel, dim3((gu_waves + 3) / 4, a.k + 1), dim3(256), 0, s,
-                       a);
+    hipLaunchKernelGGL(decode_gate_up_kernel, dim3((a.I + 3) / 4, a.k + 1), dim3(256), 0, s, a);
     trace_point(s);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds = sizeof(uint16_t) * (size_t)(a.k + 1) * a.I;
-    static bool big_lds = false;  // (k+1) * inter bf16 may exceed the 64 KiB default
-    if (lds > 65536 && !big_lds) {
-        err = hipFuncSetAttribute((const void*)decode_down_kernel,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (err != hipSuccess) return err;
-        big_lds = true;
-    }
-    const int dn_waves = (a.d + kDnRows - 1) / kDnRows;
-    hipLaunchKernelGGL(decode_down_kernel, dim3((dn_waves + 3) / 4), dim3(256), lds, s, a);
+    hipLaunchKernelGGL(decode_down_kernel, dim3((a.d + 3) / 4), dim3(256), 0, s, a);
     trace_point(s);
     return hipGetLastError();
 }

@@ -123,6 +123,27 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Sum of v over the wave, returned to every lane, in a fixed order: four DPP
+// steps leave every lane with the sum of its row of 16 lanes (add the
+// neighbour, the other pair, the mirrored quad, the mirrored half row), then
+// the four row sums are added through scalar registers.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
+    v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
+    v += dpp_f32<0x141>(v);  // row_half_mirror
+    v += dpp_f32<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {

@@ -36,7 +36,7 @@ def test_header_limits_match_binding():
     text = open(HEADER).read()
     for name in ("MOE_GROUP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_TOKENS", "MOE_MAX_D",
                  "MOE_MAX_INTER", "MOE_BLOCK_ROWS", "MOE_TILE_ROWS", "MOE_ROUTE_BLOCK",
-                 "MOE_LOGITS_IN"):
+                 "MOE_DECODE_ROUTER_ROWS", "MOE_LOGITS_IN"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m, name
         if hasattr(_abi, name):
