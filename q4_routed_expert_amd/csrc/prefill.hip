@@ -116,8 +116,26 @@ __device__ __forceinline__ void down_store(const PrefillArgs& a, int shared, int
 // for every older one), which would collapse the prefetch pipeline.
 struct BChunk {
     u32x4 lo, hi;
-    uint32_t s0, b0, s1, b1;
+    uint32_t sp, bp;  // scales / biases of the two groups (low half = the group of lo)
 };
+
+// Loads one lane's share of a weight chunk (row wrow, k from kc0 and kc1).
+// With an even number of groups per row the two groups' scales (and biases)
+// are one aligned 32-bit load; otherwise two 16-bit loads each.
+__device__ __forceinline__ void load_bchunk(const Q4& W, size_t wrow, int K, int kc0, int kc1,
+                                            int half, bool pair_sb, BChunk& st) {
+    const uint32_t* qrow = W.q + wrow * (K / 8) + 4 * half;
+    const size_t grow = wrow * (K / kGroup);
+    st.lo = *(const u32x4*)(qrow + kc0 / 8);
+    st.hi = *(const u32x4*)(qrow + kc1 / 8);
+    if (pair_sb) {
+        st.sp = *(const uint32_t*)(W.scale + grow + kc0 / kGroup);
+        st.bp = *(const uint32_t*)(W.bias + grow + kc0 / kGroup);
+    } else {
+        st.sp = (uint32_t)W.scale[grow + kc0 / kGroup] | ((uint32_t)W.scale[grow + kc1 / kGroup] << 16);
+        st.bp = (uint32_t)W.bias[grow + kc0 / kGroup] | ((uint32_t)W.bias[grow + kc1 / kGroup] << 16);
+    }
+}
 
 // Any inter (a multiple of 64): the activation tile streams through LDS one
 // K-chunk at a time, double buffered, one barrier per chunk; each wave owns
@@ -190,17 +208,11 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
             *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = ok ? areg[p] : z;
         }
     };
+    const bool pair_sb = (K / kGroup) % 2 == 0;
     auto load_b = [&](int c, BChunk& st) {
         const int kc0 = c * kKC < K ? c * kKC : 0;  // clamped: always a valid chunk
         const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
-        const uint32_t* qrow = W.q + wrow * (K / 8) + 4 * half;
-        const size_t grow = wrow * (K / kGroup);
-        st.lo = *(const u32x4*)(qrow + kc0 / 8);
-        st.hi = *(const u32x4*)(qrow + kc1 / 8);
-        st.s0 = W.scale[grow + kc0 / kGroup];
-        st.b0 = W.bias[grow + kc0 / kGroup];
-        st.s1 = W.scale[grow + kc1 / kGroup];
-        st.b1 = W.bias[grow + kc1 / kGroup];
+        load_bchunk(W, wrow, K, kc0, kc1, half, pair_sb, st);
     };
 
     f32x16 acc[4];
@@ -215,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
         const unsigned char* tile = lds + buf * kTileBytes;
         // chunks (or second halves) past K contribute zero weights
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-        const float s0 = ok0 ? dq_scale(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
-        const float s1 = ok1 ? dq_scale(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
+        const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f, b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
+        const float s1 = ok1 ? dq_scale(st.sp >> 16) : 0.0f, b1 = ok1 ? bf16_to_f32(st.bp >> 16) : 0.0f;
         const int arow = lane & 31;
         bf16x8 Acur[NMS], Anxt[NMS];
 #pragma unroll
@@ -320,6 +332,7 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     const int n_ms = (M + 31) >> 5;
     constexpr int nq = kDnBlocks * nk;  // chunks this wave streams
     auto wcol0_of = [&](int blk) { return cb * (256 * kDnBlocks) + 256 * blk + 32 * wave; };
+    const bool pair_sb = (K / kGroup) % 2 == 0;
     auto load_b = [&](int q, BChunk& st) {
         const int qq = q < nq ? q : nq - 1;  // clamped: always a valid chunk
         const int blk = qq / nk, c = qq - blk * nk;
@@ -327,44 +340,36 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
         const size_t wrow = (size_t)it.e * Nw + (wc < Nw ? wc + (lane & 31) : 0);
         const int kc0 = c * kKC < K ? c * kKC : 0;
         const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
-        const uint32_t* qrow = W.q + wrow * (K / 8) + 4 * half;
-        const size_t grow = wrow * (K / kGroup);
-        st.lo = *(const u32x4*)(qrow + kc0 / 8);
-        st.hi = *(const u32x4*)(qrow + kc1 / 8);
-        st.s0 = W.scale[grow + kc0 / kGroup];
-        st.b0 = W.bias[grow + kc0 / kGroup];
-        st.s1 = W.scale[grow + kc1 / kGroup];
-        st.b1 = W.bias[grow + kc1 / kGroup];
+        load_bchunk(W, wrow, K, kc0, kc1, half, pair_sb, st);
     };
     BChunk bst[kStages];
 #pragma unroll
     for (int u = 0; u < kStages - 1; ++u) load_b(u, bst[u]);
 
-    // resident activation tile: row r, 16-byte slot s at r * row_bytes + ((s ^ (r & 15)) << 4);
-    // rows past M and columns past K are zero
+    // resident activation tile: row r, 16-byte slot s at r * row_bytes + ((s ^ (r & 15)) << 4).
+    // All of a lane's loads are issued before any store (one round trip).
+    // Rows past M hold copies of row 0 (finite; their products are never
+    // stored); columns past K are zero (their weights are zeroed too, and a
+    // zero weight times a finite value must stay zero).
     {
         constexpr int slots = nk * kSlots;  // 16-byte slots per row (K padded to the chunk)
-        constexpr int total = kMT * slots;
-        static_assert(total % (kThreads * 4) == 0, "resident tile split");
-        for (int i0 = 0; i0 < total; i0 += kThreads * 4) {
-            u32x4 v[4];
+        constexpr int per = kMT * slots / kThreads;
+        static_assert(kMT * slots % kThreads == 0, "resident tile split");
+        u32x4 v[per];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int i = i0 + tid + kThreads * p;
-                const int row = i / slots, slot = i - row * slots;
-                const int kcol = 8 * slot;
-                const bool ok = row < M && kcol < K;
-                const size_t off = (size_t)(ok ? row0 + row : 0) * K + (ok ? kcol : 0);
-                v[p] = *(const u32x4*)(A + off);
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                v[p] = ok ? v[p] : z;
-            }
+        for (int p = 0; p < per; ++p) {
+            const int i = tid + kThreads * p;
+            const int row = i / slots, slot = i - row * slots;
+            const int kcol = 8 * slot;
+            const size_t off = (size_t)(row0 + (row < M ? row : 0)) * K + (kcol < K ? kcol : 0);
+            v[p] = *(const u32x4*)(A + off);
+        }
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int i = i0 + tid + kThreads * p;
-                const int row = i / slots, slot = i - row * slots;
-                *(u32x4*)(lds + row * row_bytes + ((slot ^ (row & 15)) << 4)) = v[p];
-            }
+        for (int p = 0; p < per; ++p) {
+            const int i = tid + kThreads * p;
+            const int row = i / slots, slot = i - row * slots;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *(u32x4*)(lds + row * row_bytes + ((slot ^ (row & 15)) << 4)) = 8 * slot < K ? v[p] : z;
         }
     }
     __syncthreads();
@@ -390,8 +395,8 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     auto compute = [&](auto nms_tag, int c, const BChunk& st) {
         constexpr int NMS = decltype(nms_tag)::value;
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-        const float s0 = ok0 ? dq_scale(st.s0) : 0.0f, b0 = ok0 ? bf16_to_f32(st.b0) : 0.0f;
-        const float s1 = ok1 ? dq_scale(st.s1) : 0.0f, b1 = ok1 ? bf16_to_f32(st.b1) : 0.0f;
+        const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f, b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
+        const float s1 = ok1 ? dq_scale(st.sp >> 16) : 0.0f, b1 = ok1 ? bf16_to_f32(st.bp >> 16) : 0.0f;
         const int arow = lane & 31, sbase = c * kSlots;
         auto aread = [&](int ms, int slot) {
             const int row = 32 * ms + arow;
