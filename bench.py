@@ -97,6 +97,48 @@ def prefill_work(T, d, I, E, k, counts):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gate_up_T2048_decode.md")
+KERNEL_SOURCES = ("q4_routed_expert_amd/csrc/prefill.hip", "q4_routed_expert_amd/csrc/decode.hip",
+                  "q4_routed_expert_amd/csrc/q4moe_dev.h", "q4_routed_expert_amd/csrc/internal.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
+    when the summary is missing or the kernel sources have changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("source_hash") == kernel_source_hash() and key in rec:
+                        return rec[key]
+    except OSError:
+        pass
+    return None
+
+
+def copy_calibration(torch):
+    """A plain copy of known size for calibrating the HBM byte counters: reads and writes
+    256 MiB once per call (an elementwise negation, one kernel)."""
+    n = 64 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x elementwise negation of {4 * n} bytes")
+    del src, dst
+
+
 def roofline(flops, nbytes, seconds):
     t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
     t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
@@ -172,6 +214,7 @@ def bench_prefill(args, q4, torch, ev, stream):
     gu_sec = per["gate_up"] / 1e3
     out["roofline"] = roofline(work["gate_up"]["flops"], work["gate_up"]["bytes"], gu_sec)
     out["roofline"]["kernel"] = "gate_up_kernel (grouped gate/up GEMM + SiLU*up)"
+    out["roofline"]["traffic"] = measured_traffic("gate_up_bytes")
     out["roofline"]["mfma_frac"] = round(work["gate_up"]["flops"] / gu_sec / 1e12 / PEAK_BF16_TFLOPS, 4)
     del layers, ws
     torch.cuda.empty_cache()
@@ -254,7 +297,8 @@ def bench_decode(args, q4, torch, ev, stream):
     k_sec = sum(per.values()) / 1e6
     out["roofline"] = {"bound": "hbm", "achieved": round(ex_bytes / k_sec / 1e9, 1),
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
+                       "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4),
+                       "traffic": measured_traffic("decode_bytes_per_layer"),
                        "kernels": "decode router partial + router top-k + gate/up + down/combine"}
     del layers, ws
     torch.cuda.empty_cache()
@@ -289,6 +333,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB copy (for HBM byte-counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -303,6 +349,8 @@ def main():
         sys.exit(2)
     ev = HipEvents()
     stream = int(torch.cuda.current_stream().cuda_stream)
+    if args.copy_calibration:
+        copy_calibration(torch)
     pre = bench_prefill(args, q4, torch, ev, stream)
     dec = None if args.no_decode else bench_decode(args, q4, torch, ev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
