@@ -490,13 +490,19 @@ __device__ __forceinline__ UnitDesc uniform_desc(const UnitDesc& d) {
     return u;
 }
 
-// One lane's share of one weight chunk with the scale and bias of both
-// groups packed as pairs (low half = the group of lo, high half = hi).
+// One lane's share of one weight chunk: the codes of k in [kc + 32h, +32)
+// and [kc + 64 + 32h, +32) (h = lane / 32), and -- when scales and biases are
+// loaded per chunk -- the two groups' scale and bias pairs (low half = the
+// group of lo).
 struct WChunk {
     u32x4 lo, hi;
     uint32_t sp, bp;
 };
 
+// kSB4: every row has a multiple of 8 groups (K % 512 == 0), so one 16-byte
+// load brings a lane the scales (or biases) of four consecutive chunks; they
+// are loaded once per four chunks instead of once per chunk.
+template <bool kSB4>
 __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a, const int n_cb) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
     __shared__ UnitDesc s_unit[kBatch];
@@ -517,11 +523,14 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
 
     f32x16 acc[4];
     WChunk bst[kStages];
+    u32x4 s4c, b4c, s4n, b4n;                  // kSB4: scales / biases of this and the next 4 chunks
     u32x4 ast[kGuALoads];                      // the activation chunk after the current one
     uint32_t a_row[kGuALoads];                 // activation stream: row offsets of its unit
     const uint32_t* w_q = nullptr;             // weight stream: this lane's row in its unit
     const uint16_t* w_s = nullptr;
     const uint16_t* w_b = nullptr;
+    const uint16_t* v_s = nullptr;             // scale/bias stream (kSB4): its own unit
+    const uint16_t* v_b = nullptr;
 
     int u_next = g;
     while (true) {
@@ -557,31 +566,33 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
         }
         if (nb == 0) break;
         __syncthreads();
-        int a_unit = -1, w_unit = -1;
+        int a_unit = -1, w_unit = -1, v_unit = -1;
 
         // ---- loaders (clamped to valid addresses, never under a branch) ----
         // Rows past M were given source row 0 in the descriptor (their products
         // are never stored), and columns at or past K read a column of the same
         // row below 64 (their weights are zeroed in compute), so every load
-        // stays inside x.  The activation and weight streams each keep the
-        // per-lane addresses of the unit they are reading in registers and
-        // refresh them from LDS only when they cross into the next unit, so
-        // the per-chunk work is a few adds.
-        auto load_a = [&](int sp, u32x4 (&areg)[kGuALoads]) {
+        // stays inside x.  Each stream keeps the per-lane addresses of the unit
+        // it is reading in registers and refreshes them from LDS only when it
+        // crosses into the next unit, so the per-chunk work is a few adds.
+        // Activation load p of a lane covers tile rows 32p..32p+31 (subtile p),
+        // so a unit with NMS subtiles needs loads 0..NMS-1 only.
+        auto a_refresh = [&](int sp) {
             sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
-            const int bb = sp / NL, c = sp - bb * NL;
+            const int bb = sp / NL;
             if (bb != a_unit) {  // uniform: once per unit
                 a_unit = bb;
 #pragma unroll
                 for (int p = 0; p < kGuALoads; ++p)
                     a_row[p] = (uint32_t)s_src[bb][(tid + kGuThreads * p) >> 4] * (uint32_t)K;
             }
-            const int kc = c * kKC + 8 * (tid & 15);
-            const uint32_t col = kc < K ? (uint32_t)kc : (uint32_t)(kc & 63);
-#pragma unroll
-            for (int p = 0; p < kGuALoads; ++p) areg[p] = *(const u32x4*)(a.x + (a_row[p] + col));
+            const int kc = (sp - bb * NL) * kKC + 8 * (tid & 15);
+            return kc < K ? (uint32_t)kc : (uint32_t)(kc & 63);
         };
-        auto load_b = [&](int sp, WChunk& st) {
+        auto load_a = [&](uint32_t col, int p) {
+            ast[p] = *(const u32x4*)(a.x + (a_row[p] + col));
+        };
+        auto w_refresh = [&](int sp) {
             sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
             const int bb = sp / NL, c = sp - bb * NL;
             if (bb != w_unit) {  // uniform: once per unit
@@ -592,20 +603,36 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 const bool sh = ud.shared != 0;
                 const uint32_t* gq = sh ? a.sh_gate.q : a.gate.q;
                 const uint32_t* uq = sh ? a.sh_up.q : a.up.q;
-                const uint16_t* gs = sh ? a.sh_gate.scale : a.gate.scale;
-                const uint16_t* us = sh ? a.sh_up.scale : a.up.scale;
-                const uint16_t* gb = sh ? a.sh_gate.bias : a.gate.bias;
-                const uint16_t* ub = sh ? a.sh_up.bias : a.up.bias;
                 const int j0 = ud.cb * kGuCols + 16 * wave;
                 const size_t wrow = (size_t)ud.e * Nw + (j0 < Nw ? j0 + jrow : 0);
                 w_q = (is_up ? uq : gq) + wrow * (K / 8) + 4 * half;
-                w_s = (is_up ? us : gs) + wrow * (K / kGroup);
-                w_b = (is_up ? ub : gb) + wrow * (K / kGroup);
+                if (!kSB4) {
+                    const uint16_t* gs = sh ? a.sh_gate.scale : a.gate.scale;
+                    const uint16_t* us = sh ? a.sh_up.scale : a.up.scale;
+                    const uint16_t* gb = sh ? a.sh_gate.bias : a.gate.bias;
+                    const uint16_t* ub = sh ? a.sh_up.bias : a.up.bias;
+                    w_s = (is_up ? us : gs) + wrow * (K / kGroup);
+                    w_b = (is_up ? ub : gb) + wrow * (K / kGroup);
+                }
             }
+            return c;
+        };
+        auto load_w_lo = [&](int c, WChunk& st) {
+            const int kc0 = c * kKC < K ? c * kKC : 0;
+            st.lo = *(const u32x4*)(w_q + kc0 / 8);
+        };
+        auto load_w_hi = [&](int c, WChunk& st) {
             const int kc0 = c * kKC < K ? c * kKC : 0;
             const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
-            st.lo = *(const u32x4*)(w_q + kc0 / 8);
             st.hi = *(const u32x4*)(w_q + kc1 / 8);
+        };
+        auto load_w = [&](int c, WChunk& st) {
+            load_w_lo(c, st);
+            load_w_hi(c, st);
+        };
+        auto load_sb = [&](int c, WChunk& st) {  // !kSB4: this chunk's pairs
+            const int kc0 = c * kKC < K ? c * kKC : 0;
+            const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
             if (pair_sb) {
                 st.sp = *(const uint32_t*)(w_s + kc0 / kGroup);
                 st.bp = *(const uint32_t*)(w_b + kc0 / kGroup);
@@ -614,21 +641,48 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 st.bp = (uint32_t)w_b[kc0 / kGroup] | ((uint32_t)w_b[kc1 / kGroup] << 16);
             }
         };
-        auto store_a = [&](int buf, const u32x4 (&areg)[kGuALoads]) {
+        // kSB4: scales and biases of chunks c..c+3 of the unit holding stream
+        // position sp (c is a multiple of 4 there)
+        auto load_sb4 = [&](int sp, u32x4& s4, u32x4& b4) {
+            sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
+            const int bb = sp / NL, c = (sp - bb * NL) & ~3;  // the clamped end is no multiple of 4
+            if (bb != v_unit) {  // uniform: once per unit
+                v_unit = bb;
+                const UnitDesc ud = uniform_desc(s_unit[bb]);
+                const bool sh = ud.shared != 0;
+                const uint16_t* gs = sh ? a.sh_gate.scale : a.gate.scale;
+                const uint16_t* us = sh ? a.sh_up.scale : a.up.scale;
+                const uint16_t* gb = sh ? a.sh_gate.bias : a.gate.bias;
+                const uint16_t* ub = sh ? a.sh_up.bias : a.up.bias;
+                const int j0 = ud.cb * kGuCols + 16 * wave;
+                const size_t wrow = (size_t)ud.e * Nw + (j0 < Nw ? j0 + jrow : 0);
+                v_s = (is_up ? us : gs) + wrow * (K / kGroup);
+                v_b = (is_up ? ub : gb) + wrow * (K / kGroup);
+            }
+            s4 = *(const u32x4*)(v_s + 2 * c);
+            b4 = *(const u32x4*)(v_b + 2 * c);
+        };
+        auto store_a = [&](auto nms_tag, int buf) {
+            constexpr int NMS = decltype(nms_tag)::value;
 #pragma unroll
-            for (int p = 0; p < kGuALoads; ++p) {
+            for (int p = 0; p < NMS; ++p) {
                 const int i = tid + kGuThreads * p, row = i >> 4, slot = i & 15;
-                *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = areg[p];
+                *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = ast[p];
             }
         };
-        auto compute = [&](auto nms_tag, int c, int buf, const WChunk& st) {
+        // One chunk: 8 steps of (dequantise 8 k of the lane's weight row,
+        // NMS MFMAs).  issue(j) puts the next chunks' global loads between the
+        // steps, so that the waves of a CU do not all queue their loads at once
+        // right after the barrier.
+        auto compute = [&](auto nms_tag, int c, int buf, const WChunk& st, uint32_t sp,
+                           uint32_t bp, auto&& issue) {
             constexpr int NMS = decltype(nms_tag)::value;
             const unsigned char* tile = lds + buf * kTileBytes;
             const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-            const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f;
-            const float b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
-            const float s1 = ok1 ? dq_scale(st.sp >> 16) : 0.0f;
-            const float b1 = ok1 ? bf16_to_f32(st.bp >> 16) : 0.0f;
+            const float s0 = ok0 ? dq_scale(sp & 0xFFFFu) : 0.0f;
+            const float b0 = ok0 ? bf16_to_f32(bp & 0xFFFFu) : 0.0f;
+            const float s1 = ok1 ? dq_scale(sp >> 16) : 0.0f;
+            const float b1 = ok1 ? bf16_to_f32(bp >> 16) : 0.0f;
             // row 32*ms + lane%32 has (row & 15) == (lane & 15) for every ms, so the
             // swizzled slot offset is shared by the subtiles
             const unsigned char* trow = tile + (lane & 31) * kRowBytes;
@@ -646,6 +700,8 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                     for (int ms = 0; ms < NMS; ++ms)
                         Anxt[ms] = *(const bf16x8*)(trow + 32 * ms * kRowBytes + so);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                issue(j);
                 __builtin_amdgcn_sched_barrier(0);
                 const bf16x8 B =
                     j < 4 ? dequant8(st.lo[j & 3], s0, b0) : dequant8(st.hi[j & 3], s1, b1);
@@ -686,31 +742,79 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
         };
-        auto unit_loop = [&](auto nms_tag, int bb) {
-            const int cbu = __builtin_amdgcn_readfirstlane(s_unit[bb].cb);
-            const bool on = cbu * kGuCols + 16 * wave < Nw;
-            for (int c0 = 0; c0 < NL; c0 += kStages) {
+        // Four chunks c0..c0+3 of unit bb.  LAST: the final four, whose last
+        // chunk prefetches the next unit's first activation chunk (all four
+        // loads: that unit's subtile count is not known here).
+        auto four_chunks = [&](auto nms_tag, auto last_tag, int bb, int c0) {
+            constexpr int NMS = decltype(nms_tag)::value;
+            constexpr bool LAST = decltype(last_tag)::value != 0;
 #pragma unroll
-                for (int u = 0; u < kStages; ++u) {
-                    const int c = c0 + u, sp = bb * NL + c;
-                    store_a(u & 1, ast);
-                    __syncthreads();
-                    load_a(sp + 1, ast);  // chunk c+1 reuses the registers of chunk c
-                    // keep the activation loads older than the weight loads: the
-                    // next chunk's stores then wait for activations only
-                    __builtin_amdgcn_sched_barrier(0);
-                    load_b(sp + 2, bst[(u + 2) % kStages]);
-                    if (on) compute(nms_tag, c, u & 1, bst[u]);
-                }
+            for (int u = 0; u < kStages; ++u) {
+                const int c = c0 + u, sp = bb * NL + c;
+                store_a(nms_tag, u & 1);
+                __syncthreads();
+                const int nA = (LAST && u == kStages - 1) ? kGuALoads : NMS;
+                uint32_t col = 0;
+                int cw = 0;
+                // One global load per step at most: activations of chunk c+1
+                // in steps 0, 1, 3, 5 (as many as the subtiles need), codes of
+                // chunk c+2 in steps 2 and 4, its scales/biases in step 6.  A
+                // load instruction of the weight stream touches 32 rows, so the
+                // waves of a CU issuing several at once would queue behind each
+                // other in the texture unit.
+                auto issue = [&](int j) {
+                    if (j == 0) {
+                        col = a_refresh(sp + 1);
+                        if (0 < nA) load_a(col, 0);
+                    } else if (j == 1) {
+                        if (1 < nA) load_a(col, 1);
+                    } else if (j == 2) {
+                        cw = w_refresh(sp + 2);
+                        load_w_lo(cw, bst[(u + 2) % kStages]);
+                    } else if (j == 3) {
+                        if (2 < nA) load_a(col, 2);
+                    } else if (j == 4) {
+                        load_w_hi(cw, bst[(u + 2) % kStages]);
+                    } else if (j == 5) {
+                        if (3 < nA) load_a(col, 3);
+                    } else if (j == 6) {
+                        if (kSB4) {
+                            if (u == 2) load_sb4(sp + 2, s4n, b4n);
+                        } else {
+                            load_sb(cw, bst[(u + 2) % kStages]);
+                        }
+                    }
+                };
+                if (kSB4)
+                    compute(nms_tag, c, u & 1, bst[u], s4c[u], b4c[u], issue);
+                else
+                    compute(nms_tag, c, u & 1, bst[u], bst[u].sp, bst[u].bp, issue);
             }
+            if (kSB4) {
+                s4c = s4n;
+                b4c = b4n;
+            }
+        };
+        auto unit_loop = [&](auto nms_tag, int bb) {
+            for (int c0 = 0; c0 < NL - kStages; c0 += kStages) four_chunks(nms_tag, Int<0>{}, bb, c0);
+            four_chunks(nms_tag, Int<1>{}, bb, NL - kStages);
         };
 
         // ---- the batch: one continuous pipeline over nb units ----
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
-        load_a(0, ast);
-        load_b(0, bst[0]);
-        load_b(1, bst[1]);
+        {
+            const uint32_t col = a_refresh(0);
+#pragma unroll
+            for (int p = 0; p < kGuALoads; ++p) load_a(col, p);
+            load_w(w_refresh(0), bst[0]);
+            if (!kSB4) load_sb(0, bst[0]);
+            load_w(w_refresh(1), bst[1]);
+            if (kSB4)
+                load_sb4(0, s4c, b4c);
+            else
+                load_sb(1, bst[1]);
+        }
         for (int bb = 0; bb < nb; ++bb) {
             switch ((__builtin_amdgcn_readfirstlane(s_unit[bb].M) + 31) >> 5) {
                 case 1: unit_loop(Int<1>{}, bb); break;
@@ -743,7 +847,10 @@ static hipError_t launch_gate_up(const PrefillArgs& a, hipStream_t s) {
     const int max_units = (a.tile_bound + sh_items + 7) / 8 * 8 * n_cb;
     int grid = device_cus();
     if (grid > max_units) grid = max_units;
-    hipLaunchKernelGGL(gate_up_kernel, dim3(grid), dim3(kGuThreads), 0, s, a, n_cb);
+    if (a.d % (8 * kGroup) == 0)
+        hipLaunchKernelGGL(gate_up_kernel<true>, dim3(grid), dim3(kGuThreads), 0, s, a, n_cb);
+    else
+        hipLaunchKernelGGL(gate_up_kernel<false>, dim3(grid), dim3(kGuThreads), 0, s, a, n_cb);
     trace_point(s);
     return hipGetLastError();
 }
