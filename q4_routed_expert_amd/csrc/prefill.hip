@@ -296,62 +296,160 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
 
 // ---------------------------------------------------------------------------
 // Down projection with the activation tile resident in LDS (inter in
-// (384, 512], four K-chunks).  The whole M x inter bf16 tile of a work item
-// is loaded into LDS once behind a single barrier; then every wave streams
-// its weights through kDnBlocks blocks of 256 output columns x 4 K-chunks as
-// one continuous register pipeline (three chunks in flight), writing each
-// column block as soon as its last chunk is done.  No barrier sits in the
-// main loop.
+// (384, 512], four K-chunks), persistent.  A unit is (work item, 256-column
+// block); the units are ordered item by item (shared-expert tiles first) and
+// every work group takes one contiguous run of them, cut so that all runs
+// carry about the same estimated cost (per unit: 2 + number of 32-row
+// subtiles, the dequantisation being worth about two subtiles of MFMAs).
+// Every work group computes the same cut from the item list in LDS, with
+// integer arithmetic, so the runs tile the unit list exactly.  Consecutive
+// units of a run mostly share their item, so the M x inter bf16 activation
+// tile is loaded into LDS only when the item changes; the weights stream
+// through registers as one continuous pipeline over the whole run (three
+// chunks in flight, across unit boundaries).  Each 256-column block is
+// written as soon as its last chunk is done.
 // ---------------------------------------------------------------------------
 constexpr int kDnMaxI = 512;
-constexpr int kDnBlocks = 4;  // 256-column blocks per work group
+constexpr int kDnCols = 256;  // output columns per unit: 8 waves x 32
+constexpr int kDnMaxItems =
+    (MOE_MAX_TOKENS + kMT - 1) / kMT + MOE_MAX_TOKENS * kMaxTopK / kMT + kMaxExperts;
+
+__device__ __forceinline__ int down_unit_cost(int M) { return 2 + ((M + 31) >> 5); }
 
 __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillArgs a,
                                                                  const int sh_items,
-                                                                 const int n_items, const int n_cb,
-                                                                 const int n_wg) {
+                                                                 const int n_cb) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kMT * kDnMaxI * 2];
     __shared__ int s_dst[kMT];
-
-    const int b = blockIdx.x;
-    const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
-    const int item = L / n_cb, cb = L - item * n_cb;
-    if (item >= n_items) return;
-    DownItem it;
-    if (!down_item(a, item, sh_items, it)) return;
+    __shared__ int s_pre[kDnMaxItems + 1];  // cost of the units before item i
+    __shared__ short s_exp[kDnMaxItems];    // expert of item i, -1 for the shared expert
+    __shared__ int s_wtot[kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int G = gridDim.x, g = blockIdx.x;
     const int K = a.I, Nw = a.d;
-    const int M = it.M, row0 = it.row0;
-    const uint16_t* A = it.shared ? a.h_sh : a.h;
-    const Q4 W = it.shared ? a.sh_down : a.down;
-    constexpr int nk = kStages;  // K-chunks per column block
-    constexpr int row_bytes = nk * kRowBytes;
-    if (tid < kMT) s_dst[tid] = tid < M ? (it.shared ? row0 + tid : a.perm[row0 + tid]) : -1;
+    const int n_items = sh_items + *a.n_tiles;
 
-    const int n_ms = (M + 31) >> 5;
-    constexpr int nq = kDnBlocks * nk;  // chunks this wave streams
-    auto wcol0_of = [&](int blk) { return cb * (256 * kDnBlocks) + 256 * blk + 32 * wave; };
+    // ---- cost prefix over the items (fixed order, integer) ----
+    {
+        constexpr int kPer = (kDnMaxItems + kThreads - 1) / kThreads;
+        const int R = (n_items + kThreads - 1) / kThreads;
+        int cost[kPer];
+        int loc = 0;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int i = tid * R + r;
+            cost[r] = 0;
+            if (r < R && i < n_items) {
+                // straight-line form of down_item (every load address valid)
+                const bool sh = i < sh_items;
+                const int t = sh ? 0 : i - sh_items;
+                const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
+                const int end = sh ? a.T : a.offsets[e + 1];
+                const int M = min(kMT, end - (sh ? i * kMT : r0));
+                cost[r] = down_unit_cost(M) * n_cb;
+                s_exp[i] = (short)(sh ? -1 : e);
+            }
+            loc += cost[r];
+        }
+        int inc = loc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += v;
+        }
+        if (lane == 63) s_wtot[wave] = inc;
+        __syncthreads();
+        int run = inc - loc;
+        for (int w = 0; w < wave; ++w) run += s_wtot[w];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int i = tid * R + r;
+            if (r < R && i < n_items) s_pre[i] = run;
+            run += cost[r];
+        }
+        if (tid == kThreads - 1) s_pre[n_items] = run;
+        __syncthreads();
+    }
+    const long long C2 = 2ll * __builtin_amdgcn_readfirstlane(s_pre[n_items]);
+    // owner of unit (i, b): the run its cost midpoint falls in (uniform)
+    auto owner = [&](int i, int b) {
+        const int p0 = __builtin_amdgcn_readfirstlane(s_pre[i]);
+        const int p1 = __builtin_amdgcn_readfirstlane(s_pre[i + 1]);
+        const int uc = (p1 - p0) / n_cb;
+        const long long mid = 2ll * p0 + (long long)(2 * b + 1) * uc;
+        return (int)(mid * G / C2);
+    };
+    // first unit of this run: the first item whose last unit is owned by g or
+    // a later run, then the first of its blocks owned by g
+    int u_item, u_blk = 0;
+    {
+        int lo = 0, hi = n_items;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (owner(mid, n_cb - 1) >= g) hi = mid;
+            else lo = mid + 1;
+        }
+        u_item = lo;
+        if (u_item < n_items)
+            while (owner(u_item, u_blk) < g) ++u_blk;
+    }
+    u_item = __builtin_amdgcn_readfirstlane(u_item);
+    u_blk = __builtin_amdgcn_readfirstlane(u_blk);
+    auto in_run = [&](int i, int b) { return i < n_items && owner(i, b) == g; };
+    if (!in_run(u_item, u_blk)) return;  // uniform: no units for this work group
+
+    constexpr int nk = kStages;  // K-chunks per unit
+    constexpr int row_bytes = nk * kRowBytes;
     const bool pair_sb = (K / kGroup) % 2 == 0;
-    auto load_b = [&](int q, BChunk& st) {
-        const int qq = q < nq ? q : nq - 1;  // clamped: always a valid chunk
-        const int blk = qq / nk, c = qq - blk * nk;
-        const int wc = wcol0_of(blk);
-        const size_t wrow = (size_t)it.e * Nw + (wc < Nw ? wc + (lane & 31) : 0);
-        const int kc0 = c * kKC < K ? c * kKC : 0;
+
+    // ---- weight stream: a cursor over (item, block, chunk) of this run ----
+    int w_item = u_item, w_blk = u_blk, w_c = 0;
+    bool w_end = false;  // past the run: repeat the last chunk (never used)
+    auto load_next_b = [&](BChunk& st) {
+        const int e = s_exp[w_item];
+        const Q4 W = e < 0 ? a.sh_down : a.down;
+        const int wc = w_blk * kDnCols + 32 * wave;
+        const size_t wrow = (size_t)(e < 0 ? 0 : e) * Nw + (wc < Nw ? wc + (lane & 31) : 0);
+        const int kc0 = w_c * kKC < K ? w_c * kKC : 0;
         const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
         load_bchunk(W, wrow, K, kc0, kc1, half, pair_sb, st);
+        if (!w_end && ++w_c == nk) {
+            int ni = w_item, nb = w_blk + 1;
+            if (nb == n_cb) {
+                ++ni;
+                nb = 0;
+            }
+            if (in_run(ni, nb)) {
+                w_item = ni;
+                w_blk = nb;
+                w_c = 0;
+            } else {
+                w_end = true;
+                w_c = nk - 1;
+            }
+        }
     };
     BChunk bst[kStages];
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) load_b(u, bst[u]);
+    for (int u = 0; u < kStages - 1; ++u) load_next_b(bst[u]);
 
-    // resident activation tile: row r, 16-byte slot s at r * row_bytes + ((s ^ (r & 15)) << 4).
-    // All of a lane's loads are issued before any store (one round trip).
-    // Rows past M hold copies of row 0 (finite; their products are never
-    // stored); columns past K are zero (their weights are zeroed too, and a
-    // zero weight times a finite value must stay zero).
-    {
+    // ---- resident activation tile of item `item` ----
+    // row r, 16-byte slot s at r * row_bytes + ((s ^ (r & 15)) << 4).  All of
+    // a lane's loads are issued before any store (one round trip).  Rows past
+    // M hold copies of row 0 (finite; their products are never stored);
+    // columns past K are zero (their weights are zeroed too, and a zero
+    // weight times a finite value must stay zero).
+    DownItem it;
+    auto load_tile = [&](int item) {
+        down_item(a, item, sh_items, it);
+        // tid laundered here, so that the per-lane tile offsets are computed
+        // per load instead of being hoisted out of the unit loop (and spilled)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const uint16_t* A = it.shared ? a.h_sh : a.h;
+        if (tid < kMT)
+            s_dst[tid] = tid < it.M ? (it.shared ? it.row0 + tid : a.perm[it.row0 + tid]) : -1;
         constexpr int slots = nk * kSlots;  // 16-byte slots per row (K padded to the chunk)
         constexpr int per = kMT * slots / kThreads;
         static_assert(kMT * slots % kThreads == 0, "resident tile split");
@@ -361,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
             const int i = tid + kThreads * p;
             const int row = i / slots, slot = i - row * slots;
             const int kcol = 8 * slot;
-            const size_t off = (size_t)(row0 + (row < M ? row : 0)) * K + (kcol < K ? kcol : 0);
+            const size_t off = (size_t)(it.row0 + (row < it.M ? row : 0)) * K + (kcol < K ? kcol : 0);
             v[p] = *(const u32x4*)(A + off);
         }
 #pragma unroll
@@ -371,28 +469,9 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
             const u32x4 z = {0u, 0u, 0u, 0u};
             *(u32x4*)(lds + row * row_bytes + ((slot ^ (row & 15)) << 4)) = 8 * slot < K ? v[p] : z;
         }
-    }
-    __syncthreads();
-
-    f32x16 acc[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
-
-    auto epilogue = [&](int blk) __attribute__((always_inline)) {
-        const int wc = wcol0_of(blk);
-        if (wc < Nw) {
-#pragma unroll
-            for (int ms = 0; ms < 4; ++ms) {
-                const int row = 32 * ms + (lane & 31);
-                if (ms >= n_ms || row >= M) continue;
-                down_store(a, it.shared, s_dst[row], wc + 4 * half, acc[ms]);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
     };
 
-    auto compute = [&](auto nms_tag, int c, const BChunk& st) {
+    auto compute = [&](auto nms_tag, int c, const BChunk& st, f32x16 (&acc)[decltype(nms_tag)::value]) {
         constexpr int NMS = decltype(nms_tag)::value;
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
         const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f, b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
@@ -424,24 +503,47 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
         }
     };
 
-    // chunk u of every column block uses stage u, so the block loop needs no
-    // remainder handling and each column block's outputs are written once,
-    // outside the unrolled body
-    auto main_loop = [&](auto nms_tag) {
-        for (int blk = 0; blk < kDnBlocks; ++blk) {
+    // chunk c of every unit uses stage c, so each unit is one unrolled body
+    auto unit_body = [&](auto nms_tag, int blk) {
+        constexpr int NMS = decltype(nms_tag)::value;
+        const int wc = blk * kDnCols + 32 * wave;
+        f32x16 acc[NMS];  // local to the unit: not live across an activation tile load
 #pragma unroll
-            for (int u = 0; u < kStages; ++u) {
-                load_b(blk * kStages + u + kStages - 1, bst[(u + kStages - 1) % kStages]);
-                if (wcol0_of(blk) < Nw) compute(nms_tag, u, bst[u]);
+        for (int m = 0; m < NMS; ++m) acc[m] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < nk; ++c) {
+            load_next_b(bst[(c + nk - 1) % nk]);
+            if (wc < Nw) compute(nms_tag, c, bst[c], acc);
+        }
+        if (wc < Nw) {
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms) {
+                const int row = 32 * ms + (lane & 31);
+                if (row < it.M) down_store(a, it.shared, s_dst[row], wc + 4 * half, acc[ms]);
             }
-            epilogue(blk);
         }
     };
-    switch (n_ms) {
-        case 1: main_loop(Int<1>{}); break;
-        case 2: main_loop(Int<2>{}); break;
-        case 3: main_loop(Int<3>{}); break;
-        default: main_loop(Int<4>{}); break;
+
+    int cur_item = -1;
+    int ui = u_item, ub = u_blk;
+    while (true) {
+        if (ui != cur_item) {  // uniform
+            if (cur_item >= 0) __syncthreads();  // every wave is done with the old tile
+            cur_item = ui;
+            load_tile(ui);
+            __syncthreads();
+        }
+        switch ((it.M + 31) >> 5) {
+            case 1: unit_body(Int<1>{}, ub); break;
+            case 2: unit_body(Int<2>{}, ub); break;
+            case 3: unit_body(Int<3>{}, ub); break;
+            default: unit_body(Int<4>{}, ub); break;
+        }
+        if (++ub == n_cb) {
+            ++ui;
+            ub = 0;
+        }
+        if (!in_run(ui, ub)) break;
     }
 }
 
@@ -858,16 +960,18 @@ static hipError_t launch_gate_up(const PrefillArgs& a, hipStream_t s) {
 static hipError_t launch_down(const PrefillArgs& a, hipStream_t s) {
     const int sh_items = (a.T + kMT - 1) / kMT;
     const int n_items = sh_items + a.tile_bound;
-    const bool resident = (a.I + kKC - 1) / kKC == kStages;
-    const int cols_per_wg = resident ? 256 * kDnBlocks : 256;
-    const int n_cb = (a.d + cols_per_wg - 1) / cols_per_wg;
-    const int n_wg = ((n_items * n_cb) + 7) & ~7;
-    if (resident)
-        hipLaunchKernelGGL(down_resident_kernel, dim3(n_wg), dim3(kThreads), 0, s, a, sh_items,
-                           n_items, n_cb, n_wg);
-    else
+    if ((a.I + kKC - 1) / kKC == kStages) {
+        if (n_items > kDnMaxItems) return hipErrorInvalidValue;
+        const int n_cb = (a.d + kDnCols - 1) / kDnCols;
+        const int grid = min(device_cus(), n_items * n_cb);
+        hipLaunchKernelGGL(down_resident_kernel, dim3(grid), dim3(kThreads), 0, s, a, sh_items,
+                           n_cb);
+    } else {
+        const int n_cb = (a.d + 255) / 256;
+        const int n_wg = ((n_items * n_cb) + 7) & ~7;
         hipLaunchKernelGGL(down_chunked_kernel, dim3(n_wg), dim3(kThreads), 0, s, a, sh_items,
                            n_items, n_cb, n_wg);
+    }
     trace_point(s);
     return hipGetLastError();
 }
