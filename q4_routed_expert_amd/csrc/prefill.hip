@@ -50,6 +50,14 @@ struct Int {
     static constexpr int value = N;
 };
 
+// s_waitcnt vmcnt(N), leaving the other counters alone (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 __device__ __forceinline__ int lds_off(int row, int slot) {
     return row * kRowBytes + ((slot ^ (row & 15)) << 4);
 }
@@ -295,14 +303,82 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
 }
 
 // ---------------------------------------------------------------------------
+// Cost-balanced contiguous runs.  The units of a persistent GEMM are ordered
+// item by item (n_cb units per item); a unit of an item with M rows is
+// estimated to cost 2 + ceil(M / 32) (the dequantisation of its weights being
+// worth about two 32-row subtiles of MFMAs).  Every work group computes the
+// prefix of these costs in LDS (fixed order, integer) and takes the units
+// whose cost midpoints fall in its 1/G share, so the runs tile the unit list
+// exactly and carry about the same work.
+// ---------------------------------------------------------------------------
+constexpr int kMaxItems =
+    (MOE_MAX_TOKENS + kMT - 1) / kMT + MOE_MAX_TOKENS * kMaxTopK / kMT + kMaxExperts;
+
+__device__ __forceinline__ int unit_cost(int M) { return 2 + ((M + 31) >> 5); }
+
+// s_pre[i] = cost of the units of items [0, i); rows_of(i) gives item i's
+// row count (and may record per-item data).  Ends with a barrier.
+template <typename RowsOf>
+__device__ __forceinline__ void cost_prefix(int n_items, int n_cb, int* s_pre, int* s_wtot,
+                                            RowsOf&& rows_of) {
+    constexpr int kPer = (kMaxItems + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = (n_items + kThreads - 1) / kThreads;
+    int cost[kPer];
+    int loc = 0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = tid * R + r;
+        cost[r] = (r < R && i < n_items) ? unit_cost(rows_of(i)) * n_cb : 0;
+        loc += cost[r];
+    }
+    int inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+    }
+    if (lane == 63) s_wtot[wave] = inc;
+    __syncthreads();
+    int run = inc - loc;
+    for (int w = 0; w < wave; ++w) run += s_wtot[w];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = tid * R + r;
+        if (r < R && i < n_items) s_pre[i] = run;
+        run += cost[r];
+    }
+    if (tid == kThreads - 1) s_pre[n_items] = run;
+    __syncthreads();
+}
+
+// First unit (item * n_cb + block) of run g of G; n_items * n_cb for g >= G.
+__device__ __forceinline__ int run_start(int g, int G, int n_items, int n_cb, const int* s_pre) {
+    if (g >= G) return n_items * n_cb;
+    const long long C2 = 2ll * __builtin_amdgcn_readfirstlane(s_pre[n_items]);
+    auto owner = [&](int i, int b) {
+        const int p0 = __builtin_amdgcn_readfirstlane(s_pre[i]);
+        const int p1 = __builtin_amdgcn_readfirstlane(s_pre[i + 1]);
+        const long long mid = 2ll * p0 + (long long)(2 * b + 1) * ((p1 - p0) / n_cb);
+        return (int)(mid * G / C2);
+    };
+    int lo = 0, hi = n_items;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (owner(mid, n_cb - 1) >= g) hi = mid;
+        else lo = mid + 1;
+    }
+    if (lo == n_items) return n_items * n_cb;
+    int b = 0;
+    while (owner(lo, b) < g) ++b;
+    return __builtin_amdgcn_readfirstlane(lo * n_cb + b);
+}
+
+// ---------------------------------------------------------------------------
 // Down projection with the activation tile resident in LDS (inter in
 // (384, 512], four K-chunks), persistent.  A unit is (work item, 256-column
 // block); the units are ordered item by item (shared-expert tiles first) and
-// every work group takes one contiguous run of them, cut so that all runs
-// carry about the same estimated cost (per unit: 2 + number of 32-row
-// subtiles, the dequantisation being worth about two subtiles of MFMAs).
-// Every work group computes the same cut from the item list in LDS, with
-// integer arithmetic, so the runs tile the unit list exactly.  Consecutive
+// every work group takes one cost-balanced contiguous run of them.  Consecutive
 // units of a run mostly share their item, so the M x inter bf16 activation
 // tile is loaded into LDS only when the item changes; the weights stream
 // through registers as one continuous pipeline over the whole run (three
@@ -311,18 +387,14 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
 // ---------------------------------------------------------------------------
 constexpr int kDnMaxI = 512;
 constexpr int kDnCols = 256;  // output columns per unit: 8 waves x 32
-constexpr int kDnMaxItems =
-    (MOE_MAX_TOKENS + kMT - 1) / kMT + MOE_MAX_TOKENS * kMaxTopK / kMT + kMaxExperts;
-
-__device__ __forceinline__ int down_unit_cost(int M) { return 2 + ((M + 31) >> 5); }
 
 __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillArgs a,
                                                                  const int sh_items,
                                                                  const int n_cb) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kMT * kDnMaxI * 2];
     __shared__ int s_dst[kMT];
-    __shared__ int s_pre[kDnMaxItems + 1];  // cost of the units before item i
-    __shared__ short s_exp[kDnMaxItems];    // expert of item i, -1 for the shared expert
+    __shared__ int s_pre[kMaxItems + 1];  // cost of the units before item i
+    __shared__ short s_exp[kMaxItems];    // expert of item i, -1 for the shared expert
     __shared__ int s_wtot[kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
@@ -330,74 +402,21 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     const int K = a.I, Nw = a.d;
     const int n_items = sh_items + *a.n_tiles;
 
-    // ---- cost prefix over the items (fixed order, integer) ----
-    {
-        constexpr int kPer = (kDnMaxItems + kThreads - 1) / kThreads;
-        const int R = (n_items + kThreads - 1) / kThreads;
-        int cost[kPer];
-        int loc = 0;
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int i = tid * R + r;
-            cost[r] = 0;
-            if (r < R && i < n_items) {
-                // straight-line form of down_item (every load address valid)
-                const bool sh = i < sh_items;
-                const int t = sh ? 0 : i - sh_items;
-                const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
-                const int end = sh ? a.T : a.offsets[e + 1];
-                const int M = min(kMT, end - (sh ? i * kMT : r0));
-                cost[r] = down_unit_cost(M) * n_cb;
-                s_exp[i] = (short)(sh ? -1 : e);
-            }
-            loc += cost[r];
-        }
-        int inc = loc;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += v;
-        }
-        if (lane == 63) s_wtot[wave] = inc;
-        __syncthreads();
-        int run = inc - loc;
-        for (int w = 0; w < wave; ++w) run += s_wtot[w];
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int i = tid * R + r;
-            if (r < R && i < n_items) s_pre[i] = run;
-            run += cost[r];
-        }
-        if (tid == kThreads - 1) s_pre[n_items] = run;
-        __syncthreads();
-    }
-    const long long C2 = 2ll * __builtin_amdgcn_readfirstlane(s_pre[n_items]);
-    // owner of unit (i, b): the run its cost midpoint falls in (uniform)
-    auto owner = [&](int i, int b) {
-        const int p0 = __builtin_amdgcn_readfirstlane(s_pre[i]);
-        const int p1 = __builtin_amdgcn_readfirstlane(s_pre[i + 1]);
-        const int uc = (p1 - p0) / n_cb;
-        const long long mid = 2ll * p0 + (long long)(2 * b + 1) * uc;
-        return (int)(mid * G / C2);
-    };
-    // first unit of this run: the first item whose last unit is owned by g or
-    // a later run, then the first of its blocks owned by g
-    int u_item, u_blk = 0;
-    {
-        int lo = 0, hi = n_items;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (owner(mid, n_cb - 1) >= g) hi = mid;
-            else lo = mid + 1;
-        }
-        u_item = lo;
-        if (u_item < n_items)
-            while (owner(u_item, u_blk) < g) ++u_blk;
-    }
-    u_item = __builtin_amdgcn_readfirstlane(u_item);
-    u_blk = __builtin_amdgcn_readfirstlane(u_blk);
-    auto in_run = [&](int i, int b) { return i < n_items && owner(i, b) == g; };
-    if (!in_run(u_item, u_blk)) return;  // uniform: no units for this work group
+    // ---- this work group's run of units ----
+    cost_prefix(n_items, n_cb, s_pre, s_wtot, [&](int i) {
+        // straight-line form of down_item (every load address valid)
+        const bool sh = i < sh_items;
+        const int t = sh ? 0 : i - sh_items;
+        const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
+        const int end = sh ? a.T : a.offsets[e + 1];
+        s_exp[i] = (short)(sh ? -1 : e);
+        return min(kMT, end - (sh ? i * kMT : r0));
+    });
+    const int u_first = run_start(g, G, n_items, n_cb, s_pre);
+    const int u_end = run_start(g + 1, G, n_items, n_cb, s_pre);
+    if (u_first >= u_end) return;  // uniform: no units for this work group
+    const int u_item = u_first / n_cb, u_blk = u_first - u_item * n_cb;
+    auto in_run = [&](int i, int b) { return i * n_cb + b < u_end; };
 
     constexpr int nk = kStages;  // K-chunks per unit
     constexpr int row_bytes = nk * kRowBytes;
@@ -549,12 +568,10 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
 
 // ---------------------------------------------------------------------------
 // Persistent gate/up GEMM.  One work group of eight waves per CU walks a
-// static list of units (work item, 128-intermediate-column block):
-// unit u = g, g + G, ...
-// where G is the grid size.  Units are numbered so that the column blocks of
-// one item have the same index modulo 8 and therefore run on one XCD (work
-// groups are dispatched to the 8 XCDs round-robin), sharing its L2 for the
-// gathered activation rows.  The descriptors (expert, rows, source and
+// cost-balanced contiguous run of units (work item, 128-intermediate-column
+// block), ordered item by item, so the column blocks of one item mostly run
+// back to back on one CU and find the gathered activation rows in its XCD's
+// L2.  The descriptors (expert, rows, source and
 // destination rows) of up to kBatch units are computed once up front, and
 // the K-chunk pipeline then runs continuously from one unit into the next,
 // so no per-item start-up (dependent index loads) or pipeline fill/drain is
@@ -579,6 +596,26 @@ static_assert(kMT * kSlots % kGuThreads == 0, "activation tile split");
 struct UnitDesc {
     int e, row0, M, cb, shared;
 };
+
+// Vector memory operations of one gate/up wave per chunk position v of a
+// four-chunk call (v < 0: the previous call, which for FIRST is the previous
+// unit's final call): activation loads (step 0), weight codes (steps 2, 4),
+// scales/biases (step 6).
+template <bool FIRST, bool LAST, int NMS>
+constexpr int gu_n_act(int v) {
+    return v < 0 ? (FIRST ? kGuALoads : NMS) : ((LAST && v >= 1) ? kGuALoads : NMS);
+}
+template <bool SB4>
+constexpr int gu_n_sb(int v) {
+    return SB4 ? (((v + 4) & 3) == 2 ? 2 : 0) : 2;
+}
+// Operations a wave issues after its activation loads of the chunk at
+// position u (issued at position u - 3) up to the barrier of that chunk.
+template <bool SB4, bool FIRST, bool LAST, int NMS>
+constexpr int gu_ops_after(int u) {
+    return 2 + gu_n_sb<SB4>(u - 3) + gu_n_act<FIRST, LAST, NMS>(u - 2) + 2 + gu_n_sb<SB4>(u - 2) +
+           gu_n_act<FIRST, LAST, NMS>(u - 1) + 2 + gu_n_sb<SB4>(u - 1);
+}
 
 // A unit descriptor read back from LDS, moved to scalar registers: every
 // field is uniform across the work group.
@@ -606,10 +643,17 @@ struct WChunk {
 // are loaded once per four chunks instead of once per chunk.
 template <bool kSB4>
 __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a, const int n_cb) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
+    // activation ring: chunk c lives in buffer c % 4; four separate objects,
+    // so that the compiler tracks the direct-to-LDS loads into each one apart
+    __shared__ __attribute__((aligned(16))) unsigned char lds_a0[kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_a1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_a2[kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_a3[kTileBytes];
     __shared__ UnitDesc s_unit[kBatch];
     __shared__ int s_src[kBatch][kMT];
     __shared__ int s_dst[kBatch][kMT];
+    __shared__ int s_pre[kMaxItems + 1];
+    __shared__ int s_wtot[kGuWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int G = gridDim.x, g = blockIdx.x;
@@ -617,7 +661,6 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     const int n_tiles = *a.n_tiles;
     const int sh_items = (a.T + kMT - 1) / kMT;
     const int n_items = n_tiles + sh_items;
-    const int n_units = (n_items + 7) / 8 * 8 * n_cb;
     const int NL = ((K + kKC - 1) / kKC + kStages - 1) / kStages * kStages;  // chunks per unit
     const bool pair_sb = (K / kGroup) % 2 == 0;  // scale/bias pairs are 4-byte aligned
     const bool is_up = (lane & 16) != 0;         // weight row lane%32: gate j0+n or up j0+n-16
@@ -626,24 +669,33 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     f32x16 acc[4];
     WChunk bst[kStages];
     u32x4 s4c, b4c, s4n, b4n;                  // kSB4: scales / biases of this and the next 4 chunks
-    u32x4 ast[kGuALoads];                      // the activation chunk after the current one
     uint32_t a_row[kGuALoads];                 // activation stream: row offsets of its unit
+    // a lane's 16-byte piece of a staged row lands in physical slot lane & 15
+    // of tile row 4 * wave + lane / 16 (+ 32 p); it holds logical slot
+    // (lane & 15) ^ (row & 15) of the row (the XOR swizzle)
+    const int a_lslot = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
     const uint32_t* w_q = nullptr;             // weight stream: this lane's row in its unit
     const uint16_t* w_s = nullptr;
     const uint16_t* w_b = nullptr;
     const uint16_t* v_s = nullptr;             // scale/bias stream (kSB4): its own unit
     const uint16_t* v_b = nullptr;
 
-    int u_next = g;
+    // this work group's cost-balanced run of units (item * n_cb + column block)
+    cost_prefix(n_items, n_cb, s_pre, s_wtot, [&](int i) {
+        const bool sh = i >= n_tiles;
+        const int t = sh ? 0 : i;
+        const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
+        return sh ? min(kMT, a.T - (i - n_tiles) * kMT) : min(kMT, a.offsets[e + 1] - r0);
+    });
+    int u_next = run_start(g, G, n_items, n_cb, s_pre);
+    const int u_end = run_start(g + 1, G, n_items, n_cb, s_pre);
     while (true) {
-        // ---- descriptors of up to kBatch valid units ----
+        // ---- descriptors of up to kBatch units ----
         __syncthreads();  // the previous batch is done with s_unit / s_src / s_dst
         int nb = 0;
-        while (nb < kBatch && u_next < n_units) {
-            const int blk = u_next / (8 * n_cb), r = u_next - blk * 8 * n_cb;
-            const int cb = r >> 3, item = blk * 8 + (r & 7);
-            u_next += G;
-            if (item >= n_items) continue;
+        while (nb < kBatch && u_next < u_end) {
+            const int item = u_next / n_cb, cb = u_next - item * n_cb;
+            ++u_next;
             const int bi = nb++;
             int e = 0, row0, M, shared = 0;
             if (item < n_tiles) {
@@ -679,24 +731,40 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
         // crosses into the next unit, so the per-chunk work is a few adds.
         // Activation load p of a lane covers tile rows 32p..32p+31 (subtile p),
         // so a unit with NMS subtiles needs loads 0..NMS-1 only.
-        auto a_refresh = [&](int sp) {
-            sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
-            const int bb = sp / NL;
+        auto tile_of = [&](auto buf_tag) -> unsigned char* {
+            constexpr int b = decltype(buf_tag)::value & 3;
+            return b == 0 ? lds_a0 : b == 1 ? lds_a1 : b == 2 ? lds_a2 : lds_a3;
+        };
+        // Stream positions are (unit bb of the batch, chunk c), uniform; past
+        // the batch they are clamped to its last chunk (loads that are never
+        // used, at valid addresses).
+        auto clamp_pos = [&](int& bb, int& c) {
+            if (bb >= nb) {
+                bb = nb - 1;
+                c = NL - 1;
+            }
+        };
+        // column of this lane's piece of chunk (bb, c) (refreshing the row
+        // offsets when the stream enters a new unit)
+        auto a_refresh = [&](int bb, int c) {
+            clamp_pos(bb, c);
             if (bb != a_unit) {  // uniform: once per unit
                 a_unit = bb;
 #pragma unroll
                 for (int p = 0; p < kGuALoads; ++p)
                     a_row[p] = (uint32_t)s_src[bb][(tid + kGuThreads * p) >> 4] * (uint32_t)K;
             }
-            const int kc = (sp - bb * NL) * kKC + 8 * (tid & 15);
-            return kc < K ? (uint32_t)kc : (uint32_t)(kc & 63);
+            const int kc = c * kKC;
+            return kc < K ? (uint32_t)(kc + 8 * a_lslot) : (uint32_t)((8 * a_lslot) & 63);
         };
-        auto load_a = [&](uint32_t col, int p) {
-            ast[p] = *(const u32x4*)(a.x + (a_row[p] + col));
+        // direct-to-LDS load of rows 32p + 4 * wave .. +3 of an activation chunk
+        auto dma_a = [&](auto buf_tag, uint32_t col, int p) {
+            unsigned char* dst = tile_of(buf_tag) + (32 * p + 4 * wave) * kRowBytes;
+            __builtin_amdgcn_global_load_lds((const void*)(a.x + (a_row[p] + col)),
+                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         };
-        auto w_refresh = [&](int sp) {
-            sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
-            const int bb = sp / NL, c = sp - bb * NL;
+        auto w_refresh = [&](int bb, int c) {
+            clamp_pos(bb, c);
             if (bb != w_unit) {  // uniform: once per unit
                 w_unit = bb;
                 const UnitDesc ud = uniform_desc(s_unit[bb]);
@@ -743,11 +811,10 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 st.bp = (uint32_t)w_b[kc0 / kGroup] | ((uint32_t)w_b[kc1 / kGroup] << 16);
             }
         };
-        // kSB4: scales and biases of chunks c..c+3 of the unit holding stream
-        // position sp (c is a multiple of 4 there)
-        auto load_sb4 = [&](int sp, u32x4& s4, u32x4& b4) {
-            sp = __builtin_amdgcn_readfirstlane(sp < nb * NL ? sp : nb * NL - 1);
-            const int bb = sp / NL, c = (sp - bb * NL) & ~3;  // the clamped end is no multiple of 4
+        // kSB4: scales and biases of chunks c..c+3 of unit bb (c a multiple of 4)
+        auto load_sb4 = [&](int bb, int c, u32x4& s4, u32x4& b4) {
+            clamp_pos(bb, c);
+            c &= ~3;  // the clamped end is no multiple of 4
             if (bb != v_unit) {  // uniform: once per unit
                 v_unit = bb;
                 const UnitDesc ud = uniform_desc(s_unit[bb]);
@@ -764,22 +831,13 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
             s4 = *(const u32x4*)(v_s + 2 * c);
             b4 = *(const u32x4*)(v_b + 2 * c);
         };
-        auto store_a = [&](auto nms_tag, int buf) {
-            constexpr int NMS = decltype(nms_tag)::value;
-#pragma unroll
-            for (int p = 0; p < NMS; ++p) {
-                const int i = tid + kGuThreads * p, row = i >> 4, slot = i & 15;
-                *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = ast[p];
-            }
-        };
         // One chunk: 8 steps of (dequantise 8 k of the lane's weight row,
         // NMS MFMAs).  issue(j) puts the next chunks' global loads between the
         // steps, so that the waves of a CU do not all queue their loads at once
         // right after the barrier.
-        auto compute = [&](auto nms_tag, int c, int buf, const WChunk& st, uint32_t sp,
-                           uint32_t bp, auto&& issue) {
+        auto compute = [&](auto nms_tag, int c, const unsigned char* tile, const WChunk& st,
+                           uint32_t sp, uint32_t bp, auto&& issue) {
             constexpr int NMS = decltype(nms_tag)::value;
-            const unsigned char* tile = lds + buf * kTileBytes;
             const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
             const float s0 = ok0 ? dq_scale(sp & 0xFFFFu) : 0.0f;
             const float b0 = ok0 ? bf16_to_f32(bp & 0xFFFFu) : 0.0f;
@@ -789,19 +847,16 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
             // swizzled slot offset is shared by the subtiles
             const unsigned char* trow = tile + (lane & 31) * kRowBytes;
             const int sw = lane & 15;
-            bf16x8 Acur[NMS], Anxt[NMS];
-#pragma unroll
-            for (int ms = 0; ms < NMS; ++ms)
-                Acur[ms] = *(const bf16x8*)(trow + 32 * ms * kRowBytes + (((4 * half) ^ sw) << 4));
+            // each step reads its activation fragments first; the step's
+            // dequantisation covers the LDS latency
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                if (j < 7) {
-                    const int slot = (j + 1 < 4 ? 0 : 8) + 4 * half + ((j + 1) & 3);
-                    const int so = (slot ^ sw) << 4;
+                const int slot = (j < 4 ? 0 : 8) + 4 * half + (j & 3);
+                const int so = (slot ^ sw) << 4;
+                bf16x8 Af[NMS];
 #pragma unroll
-                    for (int ms = 0; ms < NMS; ++ms)
-                        Anxt[ms] = *(const bf16x8*)(trow + 32 * ms * kRowBytes + so);
-                }
+                for (int ms = 0; ms < NMS; ++ms)
+                    Af[ms] = *(const bf16x8*)(trow + 32 * ms * kRowBytes + so);
                 __builtin_amdgcn_sched_barrier(0);
                 issue(j);
                 __builtin_amdgcn_sched_barrier(0);
@@ -809,11 +864,7 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                     j < 4 ? dequant8(st.lo[j & 3], s0, b0) : dequant8(st.hi[j & 3], s1, b1);
 #pragma unroll
                 for (int ms = 0; ms < NMS; ++ms)
-                    acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B, Acur[ms], acc[ms], 0, 0, 0);
-                if (j < 7) {
-#pragma unroll
-                    for (int ms = 0; ms < NMS; ++ms) Acur[ms] = Anxt[ms];
-                }
+                    acc[ms] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B, Af[ms], acc[ms], 0, 0, 0);
             }
         };
         // h = bf16(SiLU(gate) * up): elements i (gate row) and i + 8 (up row)
@@ -844,78 +895,105 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
         };
-        // Four chunks c0..c0+3 of unit bb.  LAST: the final four, whose last
-        // chunk prefetches the next unit's first activation chunk (all four
-        // loads: that unit's subtile count is not known here).
-        auto four_chunks = [&](auto nms_tag, auto last_tag, int bb, int c0) {
+        // Four chunks c0..c0+3 of unit bb.  Activations run three chunks
+        // ahead (direct-to-LDS), weights two (registers).  FIRST / LAST: the
+        // first / final four chunks of the unit; the activation loads of the
+        // final four from the second chunk on belong to the next unit (all
+        // four loads: that unit's subtile count is not known here).
+        //
+        // The compiler does not wait for direct-to-LDS loads before LDS reads,
+        // so each wave waits for its own loads of chunk c explicitly before
+        // the barrier that publishes the chunk: vmcnt(N), N = the vector
+        // memory operations this wave issued after them, counted from the
+        // fixed issue order below (a lower bound where it is not known, which
+        // only waits longer).
+        auto four_chunks = [&](auto nms_tag, auto first_tag, auto last_tag, int bb, int c0) {
             constexpr int NMS = decltype(nms_tag)::value;
+            constexpr bool FIRST = decltype(first_tag)::value != 0;
             constexpr bool LAST = decltype(last_tag)::value != 0;
-#pragma unroll
-            for (int u = 0; u < kStages; ++u) {
-                const int c = c0 + u, sp = bb * NL + c;
-                store_a(nms_tag, u & 1);
-                __syncthreads();
-                const int nA = (LAST && u == kStages - 1) ? kGuALoads : NMS;
-                uint32_t col = 0;
+            auto step = [&](auto u_tag) {
+                constexpr int u = decltype(u_tag)::value;
+                const int c = c0 + u;
+                // stream targets: activations three chunks ahead, weights two
+                constexpr bool a_next = LAST && u >= 1, w_next = LAST && u >= 2;
+                const int a_bb = a_next ? bb + 1 : bb, a_c = a_next ? u - 1 : c + 3;
+                const int w_bb = w_next ? bb + 1 : bb, w_c = w_next ? u - 2 : c + 2;
+                constexpr int N = gu_ops_after<kSB4, FIRST, LAST, NMS>(u);
+                wait_vmcnt<N>();
+                asm volatile("s_barrier" ::: "memory");
+                constexpr int nA = (LAST && u >= 1) ? kGuALoads : NMS;
+                Int<(u + 3) & 3> nxt;
                 int cw = 0;
-                // One global load per step at most: activations of chunk c+1
-                // in steps 0, 1, 3, 5 (as many as the subtiles need), codes of
-                // chunk c+2 in steps 2 and 4, its scales/biases in step 6.  A
-                // load instruction of the weight stream touches 32 rows, so the
-                // waves of a CU issuing several at once would queue behind each
-                // other in the texture unit.
+                // step 0: this wave's activation loads of chunk c+3; steps 2
+                // and 4: codes of chunk c+2; step 6: its scales/biases
                 auto issue = [&](int j) {
                     if (j == 0) {
-                        col = a_refresh(sp + 1);
-                        if (0 < nA) load_a(col, 0);
-                    } else if (j == 1) {
-                        if (1 < nA) load_a(col, 1);
+                        const uint32_t col = a_refresh(a_bb, a_c);
+#pragma unroll
+                        for (int p = 0; p < nA; ++p) dma_a(nxt, col, p);
                     } else if (j == 2) {
-                        cw = w_refresh(sp + 2);
+                        cw = w_refresh(w_bb, w_c);
                         load_w_lo(cw, bst[(u + 2) % kStages]);
-                    } else if (j == 3) {
-                        if (2 < nA) load_a(col, 2);
                     } else if (j == 4) {
                         load_w_hi(cw, bst[(u + 2) % kStages]);
-                    } else if (j == 5) {
-                        if (3 < nA) load_a(col, 3);
                     } else if (j == 6) {
                         if (kSB4) {
-                            if (u == 2) load_sb4(sp + 2, s4n, b4n);
+                            if (u == 2) load_sb4(w_bb, w_c, s4n, b4n);
                         } else {
                             load_sb(cw, bst[(u + 2) % kStages]);
                         }
                     }
                 };
                 if (kSB4)
-                    compute(nms_tag, c, u & 1, bst[u], s4c[u], b4c[u], issue);
+                    compute(nms_tag, c, tile_of(u_tag), bst[u], s4c[u], b4c[u], issue);
                 else
-                    compute(nms_tag, c, u & 1, bst[u], bst[u].sp, bst[u].bp, issue);
-            }
+                    compute(nms_tag, c, tile_of(u_tag), bst[u], bst[u].sp, bst[u].bp, issue);
+            };
+            step(Int<0>{});
+            step(Int<1>{});
+            step(Int<2>{});
+            step(Int<3>{});
             if (kSB4) {
                 s4c = s4n;
                 b4c = b4n;
             }
         };
         auto unit_loop = [&](auto nms_tag, int bb) {
-            for (int c0 = 0; c0 < NL - kStages; c0 += kStages) four_chunks(nms_tag, Int<0>{}, bb, c0);
-            four_chunks(nms_tag, Int<1>{}, bb, NL - kStages);
+            if (NL == kStages) {
+                four_chunks(nms_tag, Int<1>{}, Int<1>{}, bb, 0);
+                return;
+            }
+            four_chunks(nms_tag, Int<1>{}, Int<0>{}, bb, 0);
+            for (int c0 = kStages; c0 < NL - kStages; c0 += kStages)
+                four_chunks(nms_tag, Int<0>{}, Int<0>{}, bb, c0);
+            four_chunks(nms_tag, Int<0>{}, Int<1>{}, bb, NL - kStages);
         };
 
         // ---- the batch: one continuous pipeline over nb units ----
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
         {
-            const uint32_t col = a_refresh(0);
+            // every wave is done with the ring (the previous batch's last chunks)
+            __syncthreads();
+            uint32_t col = a_refresh(0, 0);
 #pragma unroll
-            for (int p = 0; p < kGuALoads; ++p) load_a(col, p);
-            load_w(w_refresh(0), bst[0]);
+            for (int p = 0; p < kGuALoads; ++p) dma_a(Int<0>{}, col, p);
+            col = a_refresh(0, 1);
+#pragma unroll
+            for (int p = 0; p < kGuALoads; ++p) dma_a(Int<1>{}, col, p);
+            col = a_refresh(0, 2);
+#pragma unroll
+            for (int p = 0; p < kGuALoads; ++p) dma_a(Int<2>{}, col, p);
+            load_w(w_refresh(0, 0), bst[0]);
             if (!kSB4) load_sb(0, bst[0]);
-            load_w(w_refresh(1), bst[1]);
+            load_w(w_refresh(0, 1), bst[1]);
             if (kSB4)
-                load_sb4(0, s4c, b4c);
+                load_sb4(0, 0, s4c, b4c);
             else
                 load_sb(1, bst[1]);
+            // the per-chunk waits count from a steady pipeline; the start of a
+            // batch simply waits for everything
+            wait_vmcnt<0>();
         }
         for (int bb = 0; bb < nb; ++bb) {
             switch ((__builtin_amdgcn_readfirstlane(s_unit[bb].M) + 31) >> 5) {
@@ -961,7 +1039,7 @@ static hipError_t launch_down(const PrefillArgs& a, hipStream_t s) {
     const int sh_items = (a.T + kMT - 1) / kMT;
     const int n_items = sh_items + a.tile_bound;
     if ((a.I + kKC - 1) / kKC == kStages) {
-        if (n_items > kDnMaxItems) return hipErrorInvalidValue;
+        if (n_items > kMaxItems) return hipErrorInvalidValue;
         const int n_cb = (a.d + kDnCols - 1) / kDnCols;
         const int grid = min(device_cus(), n_items * n_cb);
         hipLaunchKernelGGL(down_resident_kernel, dim3(grid), dim3(kThreads), 0, s, a, sh_items,
