@@ -15,13 +15,14 @@ namespace q4moe {
 // x is bf16, W_r fp32.  Each W_r value is split on chip into bf16 hi + lo
 // parts (hi = bf16(w), lo = bf16(w - hi); the residual is below 2^-16 |w|) so
 // the contraction runs on bf16 MFMA with fp32 accumulation: x*hi + x*lo.
-// Work group: 64 tokens x 32 experts, four waves splitting K into quarters;
+// Work group: 64 tokens x 32 experts, eight waves splitting K into eighths;
 // each wave loads its operands straight from memory (x: 16 bytes per lane
 // per M-fragment; W_r: one fp32 per lane per k, 32 consecutive experts per
-// row = one 128-byte line) one K-step ahead of the matrix cores, and the four
+// row = one 128-byte line) a few K-steps ahead of the matrix cores, with
+// 32-bit element offsets from the uniform base pointers, and the eight
 // partial tiles are added in a fixed order through LDS at the end.
 // ---------------------------------------------------------------------------
-constexpr int kRtM = 64, kRtN = 32;
+constexpr int kRtM = 64, kRtN = 32, kRtWaves = 8;
 
 __device__ __forceinline__ void split_hi_lo(const float (&w)[8], bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -31,33 +32,43 @@ __device__ __forceinline__ void split_hi_lo(const float (&w)[8], bf16x8& hi, bf1
     }
 }
 
-__global__ __launch_bounds__(256) void router_logits_kernel(
+__global__ __launch_bounds__(64 * kRtWaves) void router_logits_kernel(
     const uint16_t* __restrict__ x, int T, int d, const float* __restrict__ W,
     const float* __restrict__ bias, int E, float* __restrict__ logits) {
     constexpr int S = 4;  // K-steps in flight per wave
-    __shared__ float red[3][2][16][64];
-    const int t0 = blockIdx.x * kRtM, e0 = blockIdx.y * kRtN;
+    __shared__ float red[kRtWaves - 1][2][16][64];
+    // Work groups go to the 8 XCDs round-robin by linear id.  Work item w =
+    // token block * n_eb + expert block, and each XCD takes one contiguous
+    // range of work items, so an XCD reads a 1/8 slice of x and all of W_r,
+    // which together fit its L2.
+    const int n_eb = (E + kRtN - 1) / kRtN;
+    const int n_wg = gridDim.x, g = blockIdx.x, xcd = g & 7;
+    int base = 0;
+    for (int xx = 0; xx < xcd; ++xx) base += (n_wg - xx + 7) >> 3;
+    const int wi = base + (g >> 3);
+    const int t0 = (wi / n_eb) * kRtM, e0 = (wi - (wi / n_eb) * n_eb) * kRtN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int n = e0 + (lane & 31);
     const bool n_ok = n < E;
-    const int kq = d / 4;  // K range of this wave (d % 64 == 0)
+    const int kq = d / kRtWaves;  // K range of this wave (d % 64 == 0: a multiple of 8)
     const int kbeg = wave * kq, kend = kbeg + kq;
-    const int n_steps = (kq / 16 + S - 1) / S * S;  // padded; steps past kend add zeros
+    const int n_steps = (kq / 16 + (kq % 16 != 0) + S - 1) / S * S;  // padded; extra steps add zeros
     const int ta = t0 + (lane & 31), tb = ta + 32;
-    // clamped, always-valid addresses: loads stay outside branches (see the
-    // grouped GEMM) and invalid values are zeroed where they are used
-    const uint16_t* xa = x + (size_t)(ta < T ? ta : 0) * d;
-    const uint16_t* xb = x + (size_t)(tb < T ? tb : 0) * d;
-    const float* wcol = W + (n_ok ? n : 0);
+    // clamped, always-valid element offsets: loads stay outside branches and
+    // invalid values are zeroed where they are used
+    const uint32_t xoa = (uint32_t)(ta < T ? ta : 0) * (uint32_t)d;
+    const uint32_t xob = (uint32_t)(tb < T ? tb : 0) * (uint32_t)d;
+    const uint32_t wo = (uint32_t)(n_ok ? n : 0);
     f32x16 acc0 = {}, acc1 = {};
     float wv[S][8];
     u32x4 av[S], bv[S];
     auto load = [&](int st, int k) {
-        const int kk = (k < kend ? k : kbeg) + 8 * half;
-        av[st] = *(const u32x4*)(xa + kk);
-        bv[st] = *(const u32x4*)(xb + kk);
+        const int kk = (k + 8 * half < kend ? k : kbeg) + 8 * half;
+        av[st] = *(const u32x4*)(x + (xoa + (uint32_t)kk));
+        bv[st] = *(const u32x4*)(x + (xob + (uint32_t)kk));
+        const uint32_t wk = wo + (uint32_t)kk * (uint32_t)E;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wv[st][i] = wcol[(size_t)(kk + i) * E];
+        for (int i = 0; i < 8; ++i) wv[st][i] = W[wk + (uint32_t)(i * E)];
     };
 #pragma unroll
     for (int u = 0; u < S - 1; ++u) load(u, kbeg + 16 * u);
@@ -65,13 +76,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
         for (int u = 0; u < S; ++u) {
             const int k = kbeg + 16 * (s0 + u);
-            const bool ok = k < kend && n_ok;
+            const bool ok = k + 8 * half < kend && n_ok;
             float w[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) w[i] = ok ? wv[u][i] : 0.0f;
             const u32x4 z = {0u, 0u, 0u, 0u};
-            const bf16x8 A0 = __builtin_bit_cast(bf16x8, ta < T ? av[u] : z);
-            const bf16x8 A1 = __builtin_bit_cast(bf16x8, tb < T ? bv[u] : z);
+            const bool okx = k + 8 * half < kend;
+            const bf16x8 A0 = __builtin_bit_cast(bf16x8, (ta < T && okx) ? av[u] : z);
+            const bf16x8 A1 = __builtin_bit_cast(bf16x8, (tb < T && okx) ? bv[u] : z);
             bf16x8 hi, lo;
             split_hi_lo(w, hi, lo);
             load((u + S - 1) % S, k + 16 * (S - 1));
@@ -94,8 +106,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = 8 * (i >> 2) + 4 * half + (i & 3);
-        const float v0 = ((acc0[i] + red[0][0][i][lane]) + red[1][0][i][lane]) + red[2][0][i][lane];
-        const float v1 = ((acc1[i] + red[0][1][i][lane]) + red[1][1][i][lane]) + red[2][1][i][lane];
+        float v0 = acc0[i], v1 = acc1[i];
+#pragma unroll
+        for (int w = 0; w < kRtWaves - 1; ++w) {
+            v0 += red[w][0][i][lane];
+            v1 += red[w][1][i][lane];
+        }
         if (t0 + r < T) logits[(size_t)(t0 + r) * E + n] = v0 + bb;
         if (t0 + 32 + r < T) logits[(size_t)(t0 + 32 + r) * E + n] = v1 + bb;
     }
@@ -103,8 +119,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 
 hipError_t launch_router_logits(const uint16_t* x, int T, int d, const float* w_router,
                                 const float* router_bias, int E, float* logits, hipStream_t s) {
-    dim3 grid((T + kRtM - 1) / kRtM, (E + kRtN - 1) / kRtN);
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, T, d, w_router,
+    const int grid = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
+    hipLaunchKernelGGL(router_logits_kernel, dim3(grid), dim3(64 * kRtWaves), 0, s, x, T, d, w_router,
                        router_bias, E, logits);
     trace_point(s);
     return hipGetLastError();
