@@ -568,10 +568,12 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
 
 // ---------------------------------------------------------------------------
 // Persistent gate/up GEMM.  One work group of eight waves per CU walks a
-// cost-balanced contiguous run of units (work item, 128-intermediate-column
-// block), ordered item by item, so the column blocks of one item mostly run
-// back to back on one CU and find the gathered activation rows in its XCD's
-// L2.  The descriptors (expert, rows, source and
+// static list of units (work item, 128-intermediate-column block), numbered
+// so that the column blocks of one item run at the same time on one XCD and
+// share its L2 for the gathered activation rows (a cost-balanced contiguous
+// run per work group, as the down kernel uses, measured slower here: the
+// column blocks of an item then run one after another and the rows are
+// fetched again).  The descriptors (expert, rows, source and
 // destination rows) of up to kBatch units are computed once up front, and
 // the K-chunk pipeline then runs continuously from one unit into the next,
 // so no per-item start-up (dependent index loads) or pipeline fill/drain is
@@ -652,8 +654,6 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     __shared__ UnitDesc s_unit[kBatch];
     __shared__ int s_src[kBatch][kMT];
     __shared__ int s_dst[kBatch][kMT];
-    __shared__ int s_pre[kMaxItems + 1];
-    __shared__ int s_wtot[kGuWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int G = gridDim.x, g = blockIdx.x;
@@ -680,22 +680,21 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     const uint16_t* v_s = nullptr;             // scale/bias stream (kSB4): its own unit
     const uint16_t* v_b = nullptr;
 
-    // this work group's cost-balanced run of units (item * n_cb + column block)
-    cost_prefix(n_items, n_cb, s_pre, s_wtot, [&](int i) {
-        const bool sh = i >= n_tiles;
-        const int t = sh ? 0 : i;
-        const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
-        return sh ? min(kMT, a.T - (i - n_tiles) * kMT) : min(kMT, a.offsets[e + 1] - r0);
-    });
-    int u_next = run_start(g, G, n_items, n_cb, s_pre);
-    const int u_end = run_start(g + 1, G, n_items, n_cb, s_pre);
+    // Units u = g, g + G, ... of the list ordered (block of 8 items, column
+    // block, item): work groups are dispatched to the 8 XCDs round-robin, so
+    // the column blocks of one item have the same u modulo 8 and run at the
+    // same time on one XCD, sharing its L2 for the gathered activation rows.
+    const int n_units = (n_items + 7) / 8 * 8 * n_cb;
+    int u_next = g;
     while (true) {
         // ---- descriptors of up to kBatch units ----
         __syncthreads();  // the previous batch is done with s_unit / s_src / s_dst
         int nb = 0;
-        while (nb < kBatch && u_next < u_end) {
-            const int item = u_next / n_cb, cb = u_next - item * n_cb;
-            ++u_next;
+        while (nb < kBatch && u_next < n_units) {
+            const int blk = u_next / (8 * n_cb), r = u_next - blk * 8 * n_cb;
+            const int cb = r >> 3, item = blk * 8 + (r & 7);
+            u_next += G;
+            if (item >= n_items) continue;
             const int bi = nb++;
             int e = 0, row0, M, shared = 0;
             if (item < n_tiles) {
