@@ -240,13 +240,13 @@ def bench_decode(args, q4, torch, ev, stream):
         q4.decode(layers[li], xs[0:1], ws, y)
     torch.cuda.synchronize()
     mid = n_steps // 2
-    ev_d = [ev.make(5) for _ in range(n_layers)]
+    ev_d = [ev.make(4) for _ in range(n_layers)]
     t = ev.make(2)
     ev.record(t[0], stream)
     for st in range(n_steps):
         for li in range(n_layers):
             if st == mid:
-                lib.moe_trace_events(C.cast(ev_d[li], C.c_void_p), 5)
+                lib.moe_trace_events(C.cast(ev_d[li], C.c_void_p), 4)
             q4.decode(layers[li], xs[st:st + 1], ws, y)
             if st == mid:
                 lib.moe_trace_events(None, 0)
@@ -254,7 +254,7 @@ def bench_decode(args, q4, torch, ev, stream):
     torch.cuda.synchronize()
     calls = n_steps * n_layers
     us_layer = ev.ms(t[0], t[1]) * 1e3 / calls
-    names = ["router_partial", "router_topk", "gate_up", "down_combine"]
+    names = ["router_shared_gate_up", "topk_gate_up", "down_combine"]
     per = {n: sum(ev.ms(ev_d[li][j], ev_d[li][j + 1]) for li in range(n_layers)) * 1e3 / n_layers
            for j, n in enumerate(names)}
     expert_bytes = (w.top_k + 1) * (2 * q4_bytes(w.inter, w.d) + q4_bytes(w.d, w.inter))
@@ -299,7 +299,7 @@ def bench_decode(args, q4, torch, ev, stream):
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                        "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4),
                        "traffic": measured_traffic("decode_bytes_per_layer"),
-                       "kernels": "decode router partial + router top-k + gate/up + down/combine"}
+                       "kernels": "decode router partials + shared gate/up, top-k + routed gate/up, down/combine"}
     del layers, ws
     torch.cuda.empty_cache()
     return out

@@ -85,8 +85,8 @@ enum {
 #define MOE_ROUTE_BLOCK 256
 
 /* moe_decode sums the router logits in partial sums over this many rows of
-   W_r (the workspace holds d / MOE_DECODE_ROUTER_ROWS x E of them). */
-#define MOE_DECODE_ROUTER_ROWS 32
+   W_r (the workspace holds ceil(d / MOE_DECODE_ROUTER_ROWS) x E of them). */
+#define MOE_DECODE_ROUTER_ROWS 128
 
 /* moe_route flag: start from the logits already in routing->logits instead of
    computing them (used to route from given fp32 logits). */
@@ -175,8 +175,8 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
 /* The whole layer for one token (T = 1): router, top-k, then dequant-GEMVs
    over the k selected experts and the shared expert with SiLU(gate)*up fused,
    then the down GEMVs fused with the scores, the shared expert and the
-   combine.  Four kernels: router partial sums; logits + top-k; gate/up;
-   down + combine.  r may be NULL; when given, r->logits [1][E], r->topk_idx [1][k]
+   combine.  Three kernels: router partial sums with the shared expert's
+   gate/up; logits + top-k with the routed gate/up; down + combine.  r may be NULL; when given, r->logits [1][E], r->topk_idx [1][k]
    and r->topk_w [1][k] are written (with MOE_LOGITS_IN, r->logits is read
    and the router is skipped).  x, y: bf16 [1][d].  ([Lily-M5] "Decode:
    minimize bytes per token".) */
@@ -192,9 +192,10 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
    before its first kernel and events[i] right after its i-th kernel, for
    i < n (moe_route: router logits, top-k, histogram, scan + scatter + maps;
    moe_prefill: gate/up, down
-   (routed and shared), combine; moe_decode: router partial sums, logits +
-   top-k, gate/up, down + combine).  With MOE_LOGITS_IN the router-logit slot is still
-   recorded but brackets no kernel.  The
+   (routed and shared), combine; moe_decode: router partial sums + shared
+   gate/up, logits + top-k + routed gate/up, down + combine).  With
+   MOE_LOGITS_IN the router-logit slot of moe_route is still recorded but
+   brackets no kernel.  The
    elapsed time between consecutive events is one kernel's duration.  events
    are hipEvent_t handles created and owned by the caller; pass NULL to stop. */
 void moe_trace_events(void* const* events, int32_t n);

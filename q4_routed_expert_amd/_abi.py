@@ -11,7 +11,7 @@ MOE_LOGITS_IN = 1
 MOE_BLOCK_ROWS = 32
 MOE_TILE_ROWS = 128
 MOE_ROUTE_BLOCK = 256
-MOE_DECODE_ROUTER_ROWS = 32
+MOE_DECODE_ROUTER_ROWS = 128
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_D, MOE_MAX_INTER = 256, 8, 32768, 8192, 2048
 
 # every function include/q4moe.h declares

@@ -107,7 +107,9 @@ DecodeWs decode_ws(const moe_layer* L) {
     w.sel_idx = o; o += align256(sizeof(int32_t) * MOE_MAX_TOPK);
     w.sel_w = o; o += align256(sizeof(float) * MOE_MAX_TOPK);
     w.logits = o; o += align256(sizeof(float) * L->n_experts);
-    w.partial = o; o += align256(sizeof(float) * (size_t)(L->d / MOE_DECODE_ROUTER_ROWS) * L->n_experts);
+    w.partial = o;
+    o += align256(sizeof(float) * (size_t)((L->d + MOE_DECODE_ROUTER_ROWS - 1) / MOE_DECODE_ROUTER_ROWS) *
+                  L->n_experts);
     w.h = o; o += align256(sizeof(uint16_t) * (size_t)(L->top_k + 1) * L->inter);
     w.total = o;
     return w;

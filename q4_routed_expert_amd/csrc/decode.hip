@@ -7,17 +7,20 @@
 // projections fused with the gate activation, the output projection fused
 // with the routing scores and the shared expert, intermediates in registers.
 //
-// Four launches on one stream, each spread over thousands of waves so that
-// the weight loads of many waves are in flight at once:
-//   1. router partial sums: d/32 work groups, each sums 32 rows of x . W_r
-//      for every expert (skipped when the logits are given);
-//   2. one work group adds the partial sums in a fixed order (four quarters
-//      in parallel, then the quarters in order), applies the bias and runs
-//      the top-k;
-//   3. gate/up: one wave per (selected or shared expert, intermediate row j):
-//      the gate and up rows are streamed once with 16-byte loads per lane and
-//      h = bf16(SiLU(g) * u) is written;
-//   4. down: one wave per output n: each lane takes one code word of each of
+// Three launches on one stream (every launch boundary costs several
+// microseconds at batch 1, so the work is packed into as few as the data
+// dependencies allow), each spread over thousands of waves so that the
+// weight loads of many waves are in flight at once:
+//   1. router partial sums (ceil(d/128) work groups, each sums 128 rows of
+//      x . W_r for every expert; skipped when the logits are given) and, in
+//      the same launch, the shared expert's gate/up rows, which need no
+//      routing;
+//   2. every work group adds the partial sums in a fixed order (+ bias) and
+//      runs the top-k itself -- the same arithmetic in every work group, so
+//      every one finds the same experts -- then computes gate/up rows of its
+//      routed slot: one wave per (slot, intermediate row j), the gate and up
+//      rows streamed once with 16-byte loads per lane, h = bf16(SiLU(g) * u);
+//   3. down: one wave per output n: each lane takes one code word of each of
 //      the k + 1 experts' rows, and the wave combines
 //      y = bf16( sum_s w_s * P_s (slot order) + P_shared ).
 // Every weight enters as the bf16 value bf16(q * s + b), the same operand the
@@ -27,88 +30,22 @@
 
 namespace q4moe {
 
-constexpr int kRouterRows = 32;  // rows of W_r per router work group (DecodeWs sizes partial by it)
+constexpr int kRouterRows = 128;  // rows of W_r per router work group (DecodeWs sizes partial by it)
 constexpr int kRouterQuarters = 4;
+constexpr int kRouterThreadRows = kRouterRows / kRouterQuarters;
+constexpr int kDecRows = 16;  // gate/up rows per 1024-thread work group, one wave each
 
 static_assert(kRouterRows == MOE_DECODE_ROUTER_ROWS, "router partial rows");
+static_assert(kRouterQuarters * kMaxExperts == 1024, "router work group shape");
 
-// Partial router sums over 32 rows of W_r: partial[g][e] = sum_j x[32g+j] W_r[32g+j][e].
-__global__ __launch_bounds__(256) void decode_router_partial_kernel(const DecodeArgs a) {
-    const int g = blockIdx.x, e = threadIdx.x, E = a.E;
-    if (e >= E) return;
-    const float* wp = a.w_router + (size_t)kRouterRows * g * E + e;
-    const uint16_t* xp = a.x + kRouterRows * g;
-    float w[kRouterRows];
-#pragma unroll
-    for (int j = 0; j < kRouterRows; ++j) w[j] = wp[(size_t)j * E];
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kRouterRows; ++j) acc = __builtin_fmaf(bf16_to_f32(xp[j]), w[j], acc);
-    a.partial[(size_t)g * E + e] = acc;
-}
-
-// Logits = partial sums added in a fixed order (+ bias), then top-k by one
-// wave.  Thread (q, e) sums the q-th quarter of expert e's partials, 16 loads
-// in flight at a time (one batch for d = 2048); the quarters are then added
-// in order.
-__global__ __launch_bounds__(1024) void decode_router_topk_kernel(const DecodeArgs a, int n_part) {
-    __shared__ float s_q[kRouterQuarters][kMaxExperts];
-    __shared__ float s_logits[kMaxExperts];
-    const int tid = threadIdx.x, E = a.E;
-    const int e = tid & (kMaxExperts - 1), q = tid / kMaxExperts;
-    if (!a.logits_in && e < E) {
-        const int per = (n_part + kRouterQuarters - 1) / kRouterQuarters;
-        const int g_beg = q * per, g_end = min(n_part, g_beg + per);
-        float v = 0.0f;
-        for (int g0 = g_beg; g0 < g_end; g0 += 16) {
-            float p[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int gg = g0 + u < g_end ? g0 + u : g_beg;  // clamped, always valid
-                p[u] = a.partial[(size_t)gg * E + e];
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) v += g0 + u < g_end ? p[u] : 0.0f;
-        }
-        s_q[q][e] = v;
-    }
-    __syncthreads();
-    if (tid < E) {
-        float v;
-        if (a.logits_in) {
-            v = a.logits[tid];
-        } else {
-            v = ((s_q[0][tid] + s_q[1][tid]) + s_q[2][tid]) + s_q[3][tid];
-            if (a.router_bias) v += a.router_bias[tid];
-            a.logits[tid] = v;
-        }
-        s_logits[tid] = v;
-    }
-    __syncthreads();
-    if (tid < 64) {
-        int se;
-        float sw;
-        wave_topk(s_logits, E, a.k, tid, &se, &sw);
-        if (tid < a.k) {
-            a.sel_idx[tid] = se;
-            a.sel_w[tid] = sw;
-            if (a.out_idx) a.out_idx[tid] = se;
-            if (a.out_w) a.out_w[tid] = sw;
-        }
-    }
-}
-
-// One wave per (slot, intermediate row j); lane covers 32 consecutive k of
-// each 2048-wide pass (half a quantisation group).  Weights are the bf16
-// values bf16(q * s + b), as in the grouped GEMM, dotted with bf16 x in fp32.
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(const DecodeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int slot = blockIdx.y;  // 0..k-1 routed, k = shared
-    if (j >= a.I) return;
+// One wave: h[slot][j] = bf16(SiLU(W_gate[e] x)_j * (W_up[e] x)_j) for expert
+// e (or the shared expert); lane covers 32 consecutive k of each 2048-wide
+// pass (half a quantisation group).  Weights are the bf16 values
+// bf16(q * s + b), as in the grouped GEMM, dotted with bf16 x in fp32.
+__device__ __forceinline__ void gate_up_row(const DecodeArgs& a, int slot, bool shared, int e,
+                                            int j, int lane) {
     const int d = a.d;
-    const bool shared = slot >= a.k;
-    const size_t row = shared ? (size_t)j : (size_t)a.sel_idx[slot] * a.I + j;
+    const size_t row = shared ? (size_t)j : (size_t)e * a.I + j;
     const uint32_t* gq = (shared ? a.sh_gate.q : a.gate.q) + row * (d / 8);
     const uint32_t* uq = (shared ? a.sh_up.q : a.up.q) + row * (d / 8);
     const uint16_t* gs = (shared ? a.sh_gate.scale : a.gate.scale) + row * (d / kGroup);
@@ -137,6 +74,92 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(const DecodeArgs a)
     }
     const float g = wave_sum_dpp(gsum), u = wave_sum_dpp(usum);
     if (lane == 0) a.h[(size_t)slot * a.I + j] = f32_to_bf16(silu(g) * u);
+}
+
+// Work groups [0, n_part): partial[g][e] = sum of x[r] W_r[r][e] over the 128
+// rows r of group g (four quarters of 32 rows summed in parallel, then the
+// quarters in order).  Work groups from n_part on: the shared expert's
+// gate/up rows, one per wave.
+__global__ __launch_bounds__(1024) void decode_router_shared_kernel(const DecodeArgs a,
+                                                                    int n_part) {
+    __shared__ float s_q[kRouterQuarters][kMaxExperts];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if ((int)blockIdx.x >= n_part) {
+        const int j = ((int)blockIdx.x - n_part) * kDecRows + wave;
+        if (j < a.I) gate_up_row(a, a.k, true, 0, j, lane);
+        return;
+    }
+    if (a.logits_in) return;  // uniform
+    const int g = blockIdx.x, E = a.E, d = a.d;
+    const int e = tid & (kMaxExperts - 1), q = tid / kMaxExperts;
+    const int r0 = g * kRouterRows + q * kRouterThreadRows;
+    const int ee = e < E ? e : 0;  // clamped, always valid
+    float w[kRouterThreadRows], xv[kRouterThreadRows];
+#pragma unroll
+    for (int r = 0; r < kRouterThreadRows; ++r) {
+        const int rr = r0 + r < d ? r0 + r : 0;
+        w[r] = a.w_router[(size_t)rr * E + ee];
+        xv[r] = bf16_to_f32(a.x[rr]);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kRouterThreadRows; ++r)
+        acc = r0 + r < d ? __builtin_fmaf(xv[r], w[r], acc) : acc;
+    s_q[q][e] = acc;
+    __syncthreads();
+    if (tid < E)
+        a.partial[(size_t)g * E + tid] = ((s_q[0][tid] + s_q[1][tid]) + s_q[2][tid]) + s_q[3][tid];
+}
+
+// Logits (partial sums added in order, + bias; or the given logits), top-k,
+// then the gate/up rows of routed slot blockIdx.y.  Work group (0, 0) also
+// writes the logits, the selection and the scores for the down kernel and
+// the caller.
+__global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeArgs a, int n_part) {
+    __shared__ float s_logits[kMaxExperts];
+    __shared__ int s_sel[kMaxTopK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, E = a.E;
+    const int slot = blockIdx.y;
+    const bool first = blockIdx.x == 0 && slot == 0;
+    if (tid < E) {
+        float v;
+        if (a.logits_in) {
+            v = a.logits[tid];
+        } else {
+            v = 0.0f;
+            for (int g0 = 0; g0 < n_part; g0 += 16) {
+                float p[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int gg = g0 + u < n_part ? g0 + u : 0;  // clamped, always valid
+                    p[u] = a.partial[(size_t)gg * E + tid];
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) v += g0 + u < n_part ? p[u] : 0.0f;
+            }
+            if (a.router_bias) v += a.router_bias[tid];
+            if (first) a.logits[tid] = v;
+        }
+        s_logits[tid] = v;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int se;
+        float sw;
+        wave_topk(s_logits, E, a.k, lane, &se, &sw);
+        if (lane < a.k) {
+            s_sel[lane] = se;
+            if (first) {
+                a.sel_idx[lane] = se;
+                a.sel_w[lane] = sw;
+                if (a.out_idx) a.out_idx[lane] = se;
+                if (a.out_w) a.out_w[lane] = sw;
+            }
+        }
+    }
+    __syncthreads();
+    const int j = blockIdx.x * kDecRows + wave;
+    if (j < a.I) gate_up_row(a, slot, false, s_sel[slot], j, lane);
 }
 
 // One wave per output n; lane covers 8 consecutive intermediate k (one code
@@ -187,15 +210,14 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-    const int n_part = a.d / kRouterRows;
-    if (!a.logits_in)
-        hipLaunchKernelGGL(decode_router_partial_kernel, dim3(n_part), dim3(256), 0, s, a);
-    trace_point(s);
-    hipLaunchKernelGGL(decode_router_topk_kernel, dim3(1), dim3(1024), 0, s, a, n_part);
+    const int n_part = (a.d + kRouterRows - 1) / kRouterRows;
+    const int n_rows = (a.I + kDecRows - 1) / kDecRows;
+    hipLaunchKernelGGL(decode_router_shared_kernel, dim3(n_part + n_rows), dim3(1024), 0, s, a,
+                       n_part);
     trace_point(s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(decode_gate_up_kernel, dim3((a.I + 3) / 4, a.k + 1), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_topk_gate_up_kernel, dim3(n_rows, a.k), dim3(1024), 0, s, a, n_part);
     trace_point(s);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

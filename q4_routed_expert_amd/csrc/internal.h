@@ -53,7 +53,7 @@ struct DecodeArgs {
     float* logits;       // [E]: written, or read when logits_in
     int32_t* out_idx;    // [k] or NULL
     float* out_w;        // [k] or NULL
-    float* partial;      // [d/MOE_DECODE_ROUTER_ROWS][E] router partial sums
+    float* partial;      // [ceil(d/MOE_DECODE_ROUTER_ROWS)][E] router partial sums
     int32_t* sel_idx;    // [k]
     float* sel_w;        // [k]
     uint16_t* h;         // bf16 [k+1][I]
