@@ -93,26 +93,50 @@ __device__ __forceinline__ bool down_item(const PrefillArgs& a, int item, int sh
 // The dequantised weights are the first MFMA operand, so the 32x32 output
 // tile is (weight row n) x (activation row): lane l holds activation row
 // l % 32 of its subtile and, in elements 4g..4g+3, the four consecutive
-// weight rows n = 8g + 4*(l/32) + 0..3.  Outputs leave in groups of four
-// consecutive columns: fp16 (8 bytes) into the routed outputs `part` (row =
-// assignment), fp32 (16 bytes) into the shared expert's `sh_out` (row = token).
-__device__ __forceinline__ void down_store(const PrefillArgs& a, int shared, int dst, int n_lane,
-                                           const f32x16& acc) {
+// weight rows n = 8g + 4h + 0..3 (h = l / 32).  Lanes l and l + 32 hold the
+// same activation row; they trade four-column groups so that each ends with
+// two runs of eight consecutive columns, 16m + 8h .. +7 for m = 0, 1, and
+// stores them whole: fp16 (16 bytes) into the routed outputs `part` (row =
+// assignment), fp32 (32 bytes) into the shared expert's `sh_out` (row =
+// token).  Both lanes of a pair take the same branches (same row).
+__device__ __forceinline__ void down_store(const PrefillArgs& a, int shared, int dst, int wc,
+                                           int half, const f32x16& acc) {
     if (shared) {
-        float* srow = a.sh_out + (size_t)dst * a.d + n_lane;
+        float* srow = a.sh_out + (size_t)dst * a.d + wc;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 v = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-            *(f32x4*)(srow + 8 * g) = v;
+        for (int m = 0; m < 2; ++m) {
+            f32x4 own_lo, own_hi, send;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                own_lo[i] = acc[4 * (2 * m) + i];      // group 2m (kept by h = 0)
+                own_hi[i] = acc[4 * (2 * m + 1) + i];  // group 2m + 1 (kept by h = 1)
+                send[i] = half ? own_lo[i] : own_hi[i];
+            }
+            f32x4 recv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) recv[i] = __shfl_xor(send[i], 32, 64);
+            const f32x4 lo = half ? recv : own_lo;
+            const f32x4 hi = half ? own_hi : recv;
+            float* o = srow + 16 * m + 8 * half;
+            *(f32x4*)o = lo;
+            *(f32x4*)(o + 4) = hi;
         }
     } else {
-        uint16_t* prow = a.part + (size_t)dst * a.d + n_lane;
+        uint16_t* prow = a.part + (size_t)dst * a.d + wc;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            uint2 v;
-            v.x = (uint32_t)f32_to_f16(acc[4 * g]) | ((uint32_t)f32_to_f16(acc[4 * g + 1]) << 16);
-            v.y = (uint32_t)f32_to_f16(acc[4 * g + 2]) | ((uint32_t)f32_to_f16(acc[4 * g + 3]) << 16);
-            *(uint2*)(prow + 8 * g) = v;
+        for (int m = 0; m < 2; ++m) {
+            uint2 own_lo, own_hi;
+            own_lo.x = (uint32_t)f32_to_f16(acc[8 * m]) | ((uint32_t)f32_to_f16(acc[8 * m + 1]) << 16);
+            own_lo.y = (uint32_t)f32_to_f16(acc[8 * m + 2]) | ((uint32_t)f32_to_f16(acc[8 * m + 3]) << 16);
+            own_hi.x = (uint32_t)f32_to_f16(acc[8 * m + 4]) | ((uint32_t)f32_to_f16(acc[8 * m + 5]) << 16);
+            own_hi.y = (uint32_t)f32_to_f16(acc[8 * m + 6]) | ((uint32_t)f32_to_f16(acc[8 * m + 7]) << 16);
+            const uint2 send = half ? own_lo : own_hi;
+            uint2 recv;
+            recv.x = (uint32_t)__shfl_xor((int)send.x, 32, 64);
+            recv.y = (uint32_t)__shfl_xor((int)send.y, 32, 64);
+            const uint2 lo = half ? recv : own_lo;
+            const uint2 hi = half ? own_hi : recv;
+            *(u32x4*)(prow + 16 * m + 8 * half) = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
     }
 }
@@ -298,7 +322,7 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
     for (int ms = 0; ms < 4; ++ms) {
         const int row = 32 * ms + (lane & 31);
         if (ms >= n_ms || row >= it.M) continue;
-        down_store(a, it.shared, s_dst[row], wcol0 + 4 * half, acc[ms]);
+        down_store(a, it.shared, s_dst[row], wcol0, half, acc[ms]);
     }
 }
 
@@ -538,7 +562,7 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
 #pragma unroll
             for (int ms = 0; ms < NMS; ++ms) {
                 const int row = 32 * ms + (lane & 31);
-                if (row < it.M) down_store(a, it.shared, s_dst[row], wc + 4 * half, acc[ms]);
+                if (row < it.M) down_store(a, it.shared, s_dst[row], wc, half, acc[ms]);
             }
         }
     };
