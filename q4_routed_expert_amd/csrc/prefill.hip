@@ -420,6 +420,9 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     __shared__ int s_pre[kMaxItems + 1];  // cost of the units before item i
     __shared__ short s_exp[kMaxItems];    // expert of item i, -1 for the shared expert
     __shared__ int s_wtot[kWaves];
+    // each wave's 32 x 32 fp16 output tile on its way to `part`: row t,
+    // 16-byte slot s at t * 64 + 16 * (s ^ ((t >> 1) & 3))
+    __shared__ __attribute__((aligned(16))) uint16_t s_out[kWaves][32 * 32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int G = gridDim.x, g = blockIdx.x;
@@ -559,10 +562,37 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
             if (wc < Nw) compute(nms_tag, c, bst[c], acc);
         }
         if (wc < Nw) {
+            if (it.shared) {
 #pragma unroll
-            for (int ms = 0; ms < NMS; ++ms) {
-                const int row = 32 * ms + (lane & 31);
-                if (row < it.M) down_store(a, it.shared, s_dst[row], wc, half, acc[ms]);
+                for (int ms = 0; ms < NMS; ++ms) {
+                    const int row = 32 * ms + (lane & 31);
+                    if (row < it.M) down_store(a, 1, s_dst[row], wc, half, acc[ms]);
+                }
+            } else {
+                // routed rows: through the wave's LDS tile, so that a store
+                // instruction writes 16 rows x 64 contiguous bytes
+                unsigned char* so = (unsigned char*)s_out[wave];
+                const int t = lane & 31;
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {  // columns 8gq + 4h .. +3: 8-byte unit 2gq + h
+                        uint2 v;
+                        v.x = (uint32_t)f32_to_f16(acc[ms][4 * gq]) |
+                              ((uint32_t)f32_to_f16(acc[ms][4 * gq + 1]) << 16);
+                        v.y = (uint32_t)f32_to_f16(acc[ms][4 * gq + 2]) |
+                              ((uint32_t)f32_to_f16(acc[ms][4 * gq + 3]) << 16);
+                        const int slot = gq ^ ((t >> 1) & 3);
+                        *(uint2*)(so + t * 64 + 16 * slot + 8 * half) = v;
+                    }
+#pragma unroll
+                    for (int pass = 0; pass < 2; ++pass) {
+                        const int r = 16 * pass + (lane >> 2), sg = lane & 3;
+                        const u32x4 v = *(const u32x4*)(so + r * 64 + 16 * (sg ^ ((r >> 1) & 3)));
+                        const int row = 32 * ms + r;
+                        if (row < it.M) *(u32x4*)(a.part + (size_t)s_dst[row] * a.d + wc + 8 * sg) = v;
+                    }
+                }
             }
         }
     };
