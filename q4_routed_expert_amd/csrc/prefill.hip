@@ -931,18 +931,26 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 for (int ms = 0; ms < 4; ++ms) {
                     const int row = 32 * ms + (lane & 31);
                     if (ms >= n_ms || row >= ud.M) continue;
-                    uint16_t* orow = out + (size_t)s_dst[bb][row] * a.I + j0 + 4 * half;
+                    // columns 8gq + 4h .. +3 per lane; lanes l and l + 32 (same
+                    // row) trade groups so each stores 8 consecutive columns
+                    uint2 own[2];
 #pragma unroll
                     for (int gq = 0; gq < 2; ++gq) {
                         float hv[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             hv[r] = silu(acc[ms][4 * gq + r]) * acc[ms][8 + 4 * gq + r];
-                        uint2 v;
-                        v.x = pack_bf16x2(hv[0], hv[1]);
-                        v.y = pack_bf16x2(hv[2], hv[3]);
-                        *(uint2*)(orow + 8 * gq) = v;
+                        own[gq].x = pack_bf16x2(hv[0], hv[1]);
+                        own[gq].y = pack_bf16x2(hv[2], hv[3]);
                     }
+                    const uint2 send = half ? own[0] : own[1];
+                    uint2 recv;
+                    recv.x = (uint32_t)__shfl_xor((int)send.x, 32, 64);
+                    recv.y = (uint32_t)__shfl_xor((int)send.y, 32, 64);
+                    const uint2 lo = half ? recv : own[0];
+                    const uint2 hi = half ? own[1] : recv;
+                    *(u32x4*)(out + (size_t)s_dst[bb][row] * a.I + j0 + 8 * half) =
+                        u32x4{lo.x, lo.y, hi.x, hi.y};
                 }
             }
 #pragma unroll
