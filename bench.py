@@ -168,7 +168,7 @@ def bench_prefill(args, q4, torch, ev, stream):
 
     def step(i, trace_route=None, trace_pre=None):
         if trace_route is not None:
-            lib.moe_trace_events(C.cast(trace_route, C.c_void_p), 5)
+            lib.moe_trace_events(C.cast(trace_route, C.c_void_p), 4)
         q4.route(layers[i % 2], xd, routing=r)
         if trace_pre is not None:
             lib.moe_trace_events(C.cast(trace_pre, C.c_void_p), 4)
@@ -179,7 +179,7 @@ def bench_prefill(args, q4, torch, ev, stream):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    ev_r = [ev.make(5) for _ in range(K)]
+    ev_r = [ev.make(4) for _ in range(K)]
     ev_p = [ev.make(4) for _ in range(K)]
     t = ev.make(2)
     torch.cuda.synchronize()
@@ -191,7 +191,7 @@ def bench_prefill(args, q4, torch, ev, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = ev.ms(t[0], t[1]) / K
-    names_r = ["router_logits", "topk", "route_count", "route_scatter"]
+    names_r = ["router_logits", "topk_histogram", "route_scatter"]
     names_p = ["gate_up", "down", "combine"]
     per = {n: 0.0 for n in names_r + names_p}
     for i in range(K):

@@ -157,7 +157,7 @@ size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
 /* Routing of T tokens, entirely on the device, no host synchronisation:
    router logits (unless MOE_LOGITS_IN), top-k selection and renormalised
    scores, histogram, exclusive scan, stable scatter into expert-sorted order,
-   and both block maps (four kernels).  x: bf16 [T][d].  ([Lily-M5] "Prefill: keep routing on
+   and both block maps (three kernels).  x: bf16 [T][d].  ([Lily-M5] "Prefill: keep routing on
    the GPU, dequantize in flight".) */
 int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
               const moe_routing* r, void* stream);
@@ -190,12 +190,11 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
 /* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill and
    moe_decode call made on this host thread records events[0] on its stream
    before its first kernel and events[i] right after its i-th kernel, for
-   i < n (moe_route: router logits, top-k, histogram, scan + scatter + maps;
+   i < n (moe_route: router logits (with MOE_LOGITS_IN: the clearing of
+   the histogram), top-k + histogram, scan + scatter + maps;
    moe_prefill: gate/up, down
    (routed and shared), combine; moe_decode: router partial sums + shared
-   gate/up, logits + top-k + routed gate/up, down + combine).  With
-   MOE_LOGITS_IN the router-logit slot of moe_route is still recorded but
-   brackets no kernel.  The
+   gate/up, logits + top-k + routed gate/up, down + combine).  The
    elapsed time between consecutive events is one kernel's duration.  events
    are hipEvent_t handles created and owned by the caller; pass NULL to stop. */
 void moe_trace_events(void* const* events, int32_t n);

@@ -173,15 +173,13 @@ int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
     if (!logits_in && (rc = check_ptr(x, "x"))) return rc;
     hipStream_t s = (hipStream_t)stream;
     trace_begin(s);
-    if (logits_in)
-        q4moe::trace_point(s);
-    else if ((rc = hip_status(q4moe::launch_router_logits(x, T, L->d, L->w_router,
-                                                          L->router_bias, L->n_experts,
-                                                          r->logits, s),
-                              "router logits")))
+    if ((rc = hip_status(q4moe::launch_router_logits(logits_in ? nullptr : x, T, L->d,
+                                                     L->w_router, L->router_bias, L->n_experts,
+                                                     r->logits, r->blk_counts, s),
+                         "router logits")))
         return rc;
     if ((rc = hip_status(q4moe::launch_topk(r->logits, T, L->n_experts, L->top_k, r->topk_idx,
-                                            r->topk_w, s),
+                                            r->topk_w, r->blk_counts, s),
                          "top-k")))
         return rc;
     return hip_status(q4moe::launch_route_sort(r->topk_idx, T, L->top_k, L->n_experts, r, s),

@@ -16,10 +16,12 @@ static_assert(MOE_ROUTE_BLOCK == 256, "the routing kernels use one thread per to
 void trace_point(hipStream_t s);
 
 // Routing ([Lily-M5] "Prefill: keep routing on the GPU, dequantize in flight").
+// x == NULL: the logits are given; only the histogram is cleared.
 hipError_t launch_router_logits(const uint16_t* x, int T, int d, const float* w_router,
-                                const float* router_bias, int E, float* logits, hipStream_t s);
+                                const float* router_bias, int E, float* logits,
+                                int32_t* blk_counts, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                       hipStream_t s);
+                       int32_t* blk_counts, hipStream_t s);
 hipError_t launch_route_sort(const int32_t* idx, int T, int k, int E, const moe_routing* r,
                              hipStream_t s);
 

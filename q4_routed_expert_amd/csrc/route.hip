@@ -1,7 +1,9 @@
 // route.hip -- GPU-resident routing of one chunk of T tokens:
 //   router logits -> top-k + renormalised scores -> histogram -> exclusive scan
 //   -> stable scatter into expert-sorted order -> 32-row block map and the
-//   128-row work map of the grouped GEMMs (four kernels).
+//   128-row work map of the grouped GEMMs (three kernels: router logits, which
+//   also clears the histogram; top-k with the histogram; scan, scatter and
+//   maps).
 // All of it stays on the device in one stream with no host synchronisation
 // ([Lily-M5] "Prefill: keep routing on the GPU, dequantize in flight": grouped
 // GEMM needs each expert's rows stored together, hence histogram, prefix scan,
@@ -34,9 +36,13 @@ __device__ __forceinline__ void split_hi_lo(const float (&w)[8], bf16x8& hi, bf1
 
 __global__ __launch_bounds__(64 * kRtWaves) void router_logits_kernel(
     const uint16_t* __restrict__ x, int T, int d, const float* __restrict__ W,
-    const float* __restrict__ bias, int E, float* __restrict__ logits) {
+    const float* __restrict__ bias, int E, float* __restrict__ logits,
+    int32_t* __restrict__ blk_counts, int n_counts) {
     constexpr int S = 4;  // K-steps in flight per wave
     __shared__ float red[kRtWaves - 1][2][16][64];
+    // the per-block expert counts that the top-k kernel accumulates start at 0
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counts; i += gridDim.x * blockDim.x)
+        blk_counts[i] = 0;
     // Work groups go to the 8 XCDs round-robin by linear id.  Work item w =
     // token block * n_eb + expert block, and each XCD takes one contiguous
     // range of work items, so an XCD reads a 1/8 slice of x and all of W_r,
@@ -117,18 +123,35 @@ __global__ __launch_bounds__(64 * kRtWaves) void router_logits_kernel(
     }
 }
 
+__global__ __launch_bounds__(256) void zero_counts_kernel(int32_t* __restrict__ blk_counts,
+                                                          int n_counts) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counts; i += gridDim.x * blockDim.x)
+        blk_counts[i] = 0;
+}
+
 hipError_t launch_router_logits(const uint16_t* x, int T, int d, const float* w_router,
-                                const float* router_bias, int E, float* logits, hipStream_t s) {
-    const int grid = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
-    hipLaunchKernelGGL(router_logits_kernel, dim3(grid), dim3(64 * kRtWaves), 0, s, x, T, d, w_router,
-                       router_bias, E, logits);
+                                const float* router_bias, int E, float* logits,
+                                int32_t* blk_counts, hipStream_t s) {
+    const int n_counts = (T + MOE_ROUTE_BLOCK - 1) / MOE_ROUTE_BLOCK * E;
+    if (!x) {  // the logits are given: only the counts are cleared
+        hipLaunchKernelGGL(zero_counts_kernel, dim3((n_counts + 255) / 256), dim3(256), 0, s,
+                           blk_counts, n_counts);
+    } else {
+        const int grid = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
+        hipLaunchKernelGGL(router_logits_kernel, dim3(grid), dim3(64 * kRtWaves), 0, s, x, T, d,
+                           w_router, router_bias, E, logits, blk_counts, n_counts);
+    }
     trace_point(s);
     return hipGetLastError();
 }
 
+// One wave per token: top-k selection and scores, and the token's k
+// assignments added to its block's expert counts (integer atomics, so the
+// counts do not depend on the order of the adds).
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
-                                                   float* __restrict__ w) {
+                                                   float* __restrict__ w,
+                                                   int32_t* __restrict__ blk_counts) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= T) return;
     int e;
@@ -137,22 +160,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     if (lane < k) {
         idx[(size_t)t * k + lane] = e;
         w[(size_t)t * k + lane] = ws;
+        atomicAdd(&blk_counts[(size_t)(t / MOE_ROUTE_BLOCK) * E + e], 1);
     }
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                       hipStream_t s) {
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+                       int32_t* blk_counts, hipStream_t s) {
+    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w,
+                       blk_counts);
     trace_point(s);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Histogram, exclusive scan, stable scatter and block maps, in two kernels
-// over blocks of kRouteBlock consecutive tokens.
-//   route_count_kernel (one work group per block): the block's per-expert
-//     assignment counts, with LDS atomic adds (integer, so order does not
-//     matter), written to blk_counts[block][E];
+// Histogram, exclusive scan, stable scatter and block maps over blocks of
+// kRouteBlock consecutive tokens.  The histogram is built by the top-k kernel
+// (each token's assignments added to blk_counts[block][E], cleared by the
+// router kernel); then
 //   route_scatter_kernel (one work group per block):
 //     1. per expert: the total count and the count of the earlier blocks
 //        (a fixed-order sum over the count table);
@@ -169,20 +193,6 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
 constexpr int kRouteBlock = MOE_ROUTE_BLOCK;
 constexpr int kRouteWaves = kRouteBlock / 64;
 static_assert(kRouteBlock % 64 == 0 && kRouteBlock >= kMaxExperts, "route block");
-
-__global__ __launch_bounds__(kRouteBlock) void route_count_kernel(const int32_t* __restrict__ idx,
-                                                                  int T, int k, int E,
-                                                                  int32_t* __restrict__ blk_counts) {
-    __shared__ int h[kMaxExperts];
-    const int tid = threadIdx.x, b = blockIdx.x;
-    if (tid < E) h[tid] = 0;
-    __syncthreads();
-    const int t = b * kRouteBlock + tid;
-    if (t < T)
-        for (int s = 0; s < k; ++s) atomicAdd(&h[idx[(size_t)t * k + s]], 1);
-    __syncthreads();
-    if (tid < E) blk_counts[(size_t)b * E + tid] = h[tid];
-}
 
 __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ blk_counts,
@@ -310,11 +320,6 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(
 hipError_t launch_route_sort(const int32_t* idx, int T, int k, int E, const moe_routing* r,
                              hipStream_t s) {
     const int n_blk = (T + kRouteBlock - 1) / kRouteBlock;
-    hipLaunchKernelGGL(route_count_kernel, dim3(n_blk), dim3(kRouteBlock), 0, s, idx, T, k, E,
-                       r->blk_counts);
-    trace_point(s);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_scatter_kernel, dim3(n_blk), dim3(kRouteBlock), 0, s, idx, T, k, E,
                        r->blk_counts, n_blk, r->counts, r->offsets, r->perm, r->inv_perm,
                        r->block_map, r->n_blocks, r->tile_map, r->n_tiles);
