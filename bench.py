@@ -329,7 +329,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-layers", type=int, default=40)
-    ap.add_argument("--cpu-tokens", type=int, default=96)
+    ap.add_argument("--cpu-tokens", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
