@@ -412,6 +412,10 @@ __device__ __forceinline__ int run_start(int g, int G, int n_items, int n_cb, co
 constexpr int kDnMaxI = 512;
 constexpr int kDnCols = 256;  // output columns per unit: 8 waves x 32
 
+// kSB4: inter % 512 == 0 (eight groups per row at most 512, so a unit's whole
+// K is one row segment): a unit's scales (and biases) are one 16-byte load
+// per lane, issued with the codes of the unit's first chunk.
+template <bool kSB4>
 __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillArgs a,
                                                                  const int sh_items,
                                                                  const int n_cb) {
@@ -452,14 +456,39 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     // ---- weight stream: a cursor over (item, block, chunk) of this run ----
     int w_item = u_item, w_blk = u_blk, w_c = 0;
     bool w_end = false;  // past the run: repeat the last chunk (never used)
-    auto load_next_b = [&](BChunk& st) {
-        const int e = s_exp[w_item];
-        const Q4 W = e < 0 ? a.sh_down : a.down;
+    u32x4 s4c = {}, b4c = {}, s4n = {}, b4n = {};  // kSB4: this unit's / the next unit's
+    // with_sb: the chunk is a unit's first (known where the call sits), so
+    // with kSB4 the unit's scales and biases come with it
+    auto load_next_b = [&](BChunk& st, u32x4& s4, u32x4& b4, auto with_sb) {
+        const int e = __builtin_amdgcn_readfirstlane(s_exp[w_item]);
+        // field by field (a per-lane select of a whole Q4 would be read from
+        // the kernel arguments through memory)
+        const bool sh = e < 0;
+        const uint32_t* Wq = sh ? a.sh_down.q : a.down.q;
+        const uint16_t* Ws = sh ? a.sh_down.scale : a.down.scale;
+        const uint16_t* Wb = sh ? a.sh_down.bias : a.down.bias;
         const int wc = w_blk * kDnCols + 32 * wave;
-        const size_t wrow = (size_t)(e < 0 ? 0 : e) * Nw + (wc < Nw ? wc + (lane & 31) : 0);
+        const size_t wrow = (size_t)(sh ? 0 : e) * Nw + (wc < Nw ? wc + (lane & 31) : 0);
         const int kc0 = w_c * kKC < K ? w_c * kKC : 0;
         const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
-        load_bchunk(W, wrow, K, kc0, kc1, half, pair_sb, st);
+        const uint32_t* qrow = Wq + wrow * (K / 8) + 4 * half;
+        st.lo = *(const u32x4*)(qrow + kc0 / 8);
+        st.hi = *(const u32x4*)(qrow + kc1 / 8);
+        if (kSB4) {
+            if (decltype(with_sb)::value) {
+                s4 = *(const u32x4*)(Ws + wrow * (K / kGroup));
+                b4 = *(const u32x4*)(Wb + wrow * (K / kGroup));
+            }
+        } else {
+            const size_t grow = wrow * (K / kGroup);
+            if (pair_sb) {
+                st.sp = *(const uint32_t*)(Ws + grow + kc0 / kGroup);
+                st.bp = *(const uint32_t*)(Wb + grow + kc0 / kGroup);
+            } else {
+                st.sp = (uint32_t)Ws[grow + kc0 / kGroup] | ((uint32_t)Ws[grow + kc1 / kGroup] << 16);
+                st.bp = (uint32_t)Wb[grow + kc0 / kGroup] | ((uint32_t)Wb[grow + kc1 / kGroup] << 16);
+            }
+        }
         if (!w_end && ++w_c == nk) {
             int ni = w_item, nb = w_blk + 1;
             if (nb == n_cb) {
@@ -477,8 +506,10 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
         }
     };
     BChunk bst[kStages];
-#pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) load_next_b(bst[u]);
+    load_next_b(bst[0], s4c, b4c, Int<1>{});
+    load_next_b(bst[1], s4c, b4c, Int<0>{});
+    load_next_b(bst[2], s4c, b4c, Int<0>{});
+    static_assert(kStages == 4, "three chunks ahead, four chunks per unit");
 
     // ---- resident activation tile of item `item` ----
     // row r, 16-byte slot s at r * row_bytes + ((s ^ (r & 15)) << 4).  All of
@@ -520,8 +551,9 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     auto compute = [&](auto nms_tag, int c, const BChunk& st, f32x16 (&acc)[decltype(nms_tag)::value]) {
         constexpr int NMS = decltype(nms_tag)::value;
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
-        const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f, b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
-        const float s1 = ok1 ? dq_scale(st.sp >> 16) : 0.0f, b1 = ok1 ? bf16_to_f32(st.bp >> 16) : 0.0f;
+        const uint32_t spv = kSB4 ? s4c[c & 3] : st.sp, bpv = kSB4 ? b4c[c & 3] : st.bp;
+        const float s0 = ok0 ? dq_scale(spv & 0xFFFFu) : 0.0f, b0 = ok0 ? bf16_to_f32(bpv & 0xFFFFu) : 0.0f;
+        const float s1 = ok1 ? dq_scale(spv >> 16) : 0.0f, b1 = ok1 ? bf16_to_f32(bpv >> 16) : 0.0f;
         const int arow = lane & 31, sbase = c * kSlots;
         auto aread = [&](int ms, int slot) {
             const int row = 32 * ms + arow;
@@ -556,10 +588,19 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
         f32x16 acc[NMS];  // local to the unit: not live across an activation tile load
 #pragma unroll
         for (int m = 0; m < NMS; ++m) acc[m] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < nk; ++c) {
-            load_next_b(bst[(c + nk - 1) % nk]);
-            if (wc < Nw) compute(nms_tag, c, bst[c], acc);
+        // the loader runs three chunks ahead, so its call at chunk 1 loads
+        // the next unit's first chunk (and scales)
+        load_next_b(bst[3], s4n, b4n, Int<0>{});
+        if (wc < Nw) compute(nms_tag, 0, bst[0], acc);
+        load_next_b(bst[0], s4n, b4n, Int<1>{});
+        if (wc < Nw) compute(nms_tag, 1, bst[1], acc);
+        load_next_b(bst[1], s4n, b4n, Int<0>{});
+        if (wc < Nw) compute(nms_tag, 2, bst[2], acc);
+        load_next_b(bst[2], s4n, b4n, Int<0>{});
+        if (wc < Nw) compute(nms_tag, 3, bst[3], acc);
+        if (kSB4) {
+            s4c = s4n;
+            b4c = b4n;
         }
         if (wc < Nw) {
             if (it.shared) {
@@ -1103,8 +1144,12 @@ static hipError_t launch_down(const PrefillArgs& a, hipStream_t s) {
         if (n_items > kMaxItems) return hipErrorInvalidValue;
         const int n_cb = (a.d + kDnCols - 1) / kDnCols;
         const int grid = min(device_cus(), n_items * n_cb);
-        hipLaunchKernelGGL(down_resident_kernel, dim3(grid), dim3(kThreads), 0, s, a, sh_items,
-                           n_cb);
+        if (a.I % (8 * kGroup) == 0)
+            hipLaunchKernelGGL(down_resident_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a,
+                               sh_items, n_cb);
+        else
+            hipLaunchKernelGGL(down_resident_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a,
+                               sh_items, n_cb);
     } else {
         const int n_cb = (a.d + 255) / 256;
         const int n_wg = ((n_items * n_cb) + 7) & ~7;
