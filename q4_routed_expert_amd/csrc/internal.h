@@ -40,6 +40,8 @@ struct PrefillArgs {
     uint16_t* h_sh;      // bf16 [T][I]
     uint16_t* part;      // fp16 [T*k][d], routed expert outputs, rows in assignment order
     float* sh_out;       // fp32 [T][d], the shared expert's outputs
+    int32_t* dn_pre;     // [items + 1] the down kernel's item cost prefix (NULL: not used)
+    int32_t* dn_exp;     // [items] the down kernel's item experts (-1: shared)
     uint16_t* y;         // bf16 [T][d]
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);

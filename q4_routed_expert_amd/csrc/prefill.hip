@@ -340,8 +340,9 @@ constexpr int kMaxItems =
 
 __device__ __forceinline__ int unit_cost(int M) { return 2 + ((M + 31) >> 5); }
 
-// s_pre[i] = cost of the units of items [0, i); rows_of(i) gives item i's
-// row count (and may record per-item data).  Ends with a barrier.
+// pre[i] = cost of the units of items [0, i) (pre in LDS or global memory);
+// rows_of(i) gives item i's row count (and may record per-item data).  Ends
+// with a barrier.
 template <typename RowsOf>
 __device__ __forceinline__ void cost_prefix(int n_items, int n_cb, int* s_pre, int* s_wtot,
                                             RowsOf&& rows_of) {
@@ -412,6 +413,26 @@ __device__ __forceinline__ int run_start(int g, int G, int n_items, int n_cb, co
 constexpr int kDnMaxI = 512;
 constexpr int kDnCols = 256;  // output columns per unit: 8 waves x 32
 
+// The down kernel's schedule: items in its order (shared-expert tiles, then the
+// routed work map), their cost prefix over (n_cb 256-column units per item)
+// and their experts (-1: shared), written to the workspace by one work group
+// of the gate/up kernel so that the down kernel's work groups only load it.
+__device__ __forceinline__ void down_schedule(const PrefillArgs& a, int* s_wtot) {
+    const int sh_items = (a.T + kMT - 1) / kMT;
+    const int n_items = sh_items + *a.n_tiles;
+    const int n_cb = (a.d + kDnCols - 1) / kDnCols;
+    cost_prefix(n_items, n_cb, a.dn_pre, s_wtot, [&](int i) {
+        // straight-line form of down_item (every load address valid)
+        const bool sh = i < sh_items;
+        const int t = sh ? 0 : i - sh_items;
+        const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
+        const int end = sh ? a.T : a.offsets[e + 1];
+        a.dn_exp[i] = sh ? -1 : e;
+        return min(kMT, end - (sh ? i * kMT : r0));
+    });
+}
+
+
 // kSB4: inter % 512 == 0 (eight groups per row at most 512, so a unit's whole
 // K is one row segment): a unit's scales (and biases) are one 16-byte load
 // per lane, issued with the codes of the unit's first chunk.
@@ -423,7 +444,6 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     __shared__ int s_dst[kMT];
     __shared__ int s_pre[kMaxItems + 1];  // cost of the units before item i
     __shared__ short s_exp[kMaxItems];    // expert of item i, -1 for the shared expert
-    __shared__ int s_wtot[kWaves];
     // each wave's 32 x 32 fp16 output tile on its way to `part`: row t,
     // 16-byte slot s at t * 64 + 16 * (s ^ ((t >> 1) & 3))
     __shared__ __attribute__((aligned(16))) uint16_t s_out[kWaves][32 * 32];
@@ -434,15 +454,13 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     const int n_items = sh_items + *a.n_tiles;
 
     // ---- this work group's run of units ----
-    cost_prefix(n_items, n_cb, s_pre, s_wtot, [&](int i) {
-        // straight-line form of down_item (every load address valid)
-        const bool sh = i < sh_items;
-        const int t = sh ? 0 : i - sh_items;
-        const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
-        const int end = sh ? a.T : a.offsets[e + 1];
-        s_exp[i] = (short)(sh ? -1 : e);
-        return min(kMT, end - (sh ? i * kMT : r0));
-    });
+    // the item cost prefix and the items' experts were computed by the
+    // gate/up kernel (down_schedule) into the workspace
+    for (int i = tid; i <= n_items; i += kThreads) {
+        s_pre[i] = a.dn_pre[i];
+        if (i < n_items) s_exp[i] = (short)a.dn_exp[i];
+    }
+    __syncthreads();
     const int u_first = run_start(g, G, n_items, n_cb, s_pre);
     const int u_end = run_start(g + 1, G, n_items, n_cb, s_pre);
     if (u_first >= u_end) return;  // uniform: no units for this work group
@@ -780,6 +798,10 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     // the column blocks of one item have the same u modulo 8 and run at the
     // same time on one XCD, sharing its L2 for the gathered activation rows.
     const int n_units = (n_items + 7) / 8 * 8 * n_cb;
+    if (a.dn_pre && g == G - 1) {  // uniform; this work group has the fewest units
+        __shared__ int s_wtot[kGuWaves];
+        down_schedule(a, s_wtot);
+    }
     int u_next = g;
     while (true) {
         // ---- descriptors of up to kBatch units ----
@@ -1123,7 +1145,16 @@ static int device_cus() {
     return cus[dev];
 }
 
-static hipError_t launch_gate_up(const PrefillArgs& a, hipStream_t s) {
+// Whether the down projection runs as down_resident_kernel, whose schedule
+// the gate/up kernel writes.
+static bool down_is_resident(const PrefillArgs& a) {
+    const int n_items = (a.T + kMT - 1) / kMT + a.tile_bound;
+    return (a.I + kKC - 1) / kKC == kStages && n_items <= kMaxItems;
+}
+
+static hipError_t launch_gate_up(const PrefillArgs& a_in, hipStream_t s) {
+    PrefillArgs a = a_in;
+    if (!down_is_resident(a)) a.dn_pre = nullptr;
     const int n_cb = (a.I + kGuCols - 1) / kGuCols;
     const int sh_items = (a.T + kMT - 1) / kMT;
     const int max_units = (a.tile_bound + sh_items + 7) / 8 * 8 * n_cb;
@@ -1141,7 +1172,7 @@ static hipError_t launch_down(const PrefillArgs& a, hipStream_t s) {
     const int sh_items = (a.T + kMT - 1) / kMT;
     const int n_items = sh_items + a.tile_bound;
     if ((a.I + kKC - 1) / kKC == kStages) {
-        if (n_items > kMaxItems) return hipErrorInvalidValue;
+        if (n_items > kMaxItems || !a.dn_pre || !a.dn_exp) return hipErrorInvalidValue;
         const int n_cb = (a.d + kDnCols - 1) / kDnCols;
         const int grid = min(device_cus(), n_items * n_cb);
         if (a.I % (8 * kGroup) == 0)
