@@ -706,6 +706,8 @@ constexpr int kGuWaves = 8;
 constexpr int kGuThreads = kGuWaves * 64;
 constexpr int kGuCols = 16 * kGuWaves;                // intermediate columns per unit
 constexpr int kGuALoads = kMT * kSlots / kGuThreads;  // 16-byte activation loads per lane per chunk
+constexpr int kGuShRows = 64;                         // rows of a shared-expert item
+constexpr bool kGuGrouped = true;
 static_assert(kMT * kSlots % kGuThreads == 0, "activation tile split");
 
 struct UnitDesc {
@@ -753,6 +755,127 @@ struct WChunk {
     uint32_t sp, bp;
 };
 
+// The items of group q of Q (item = routed tile, then the shared expert's row
+// blocks), written to s_items[0, n_run) in the order the group runs them.
+// The items are ordered by subtile count, largest first (stable inside a
+// count), and cut into Q contiguous runs at the cost midpoints: item j of the
+// order, of cost c_j = gu_unit_cost(subtiles) and cost prefix P_j, belongs to run
+// floor((2 P_j + c_j) Q / (2 P_total)).  Sorting first gives the runs with
+// heavy items fewer of them, so the runs carry about the same work even when
+// they hold only a few items each.  The order is a counting sort over the
+// four subtile counts, so every item's position and cost prefix have a closed
+// form in the class totals and its rank inside its class; every work group
+// computes only its own run.  Uniform results; contains barriers.
+constexpr int kGuPer = (kMaxItems + kGuThreads - 1) / kGuThreads;
+// estimated cost of a gate/up unit with `ms` 32-row subtiles
+__device__ __forceinline__ int gu_unit_cost(int ms) { return 2 + ms; }
+constexpr int kGuRunMax = 512;  // items one group may hold (s_items)
+
+__device__ __forceinline__ int item_run(const PrefillArgs& a, int n_tiles, int n_items, int Q,
+                                        int q, int* s_items) {
+    __shared__ int s_cls[2][kGuWaves];  // per-wave class counts, 16 bits per class
+    __shared__ int s_cnt[2][kGuWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int R = (n_items + kGuThreads - 1) / kGuThreads;
+    int cls[kGuPer];  // subtile count - 1 of each of this thread's items (-1: none)
+    int lo = 0, hi = 0;  // class counts: lo = classes 0, 1; hi = classes 2, 3
+#pragma unroll
+    for (int r = 0; r < kGuPer; ++r) {
+        const int i = tid * R + r;
+        cls[r] = -1;
+        if (r < R && i < n_items) {
+            int M;
+            if (i < n_tiles) {
+                const int e = a.tile_map[2 * i], r0 = a.tile_map[2 * i + 1];
+                M = min(kMT, a.offsets[e + 1] - r0);
+            } else {
+                M = min(kGuShRows, a.T - (i - n_tiles) * kGuShRows);
+            }
+            const int c = (M + 31) / 32 - 1;
+            cls[r] = c;
+            const int one = 1 << (16 * (c & 1));
+            lo += c < 2 ? one : 0;
+            hi += c >= 2 ? one : 0;
+        }
+    }
+    // exclusive scan of the class counts over the threads
+    int ilo = lo, ihi = hi;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int vl = __shfl_up(ilo, o, 64), vh = __shfl_up(ihi, o, 64);
+        if (lane >= o) {
+            ilo += vl;
+            ihi += vh;
+        }
+    }
+    if (lane == 63) {
+        s_cls[0][wave] = ilo;
+        s_cls[1][wave] = ihi;
+    }
+    __syncthreads();
+    int plo = ilo - lo, phi = ihi - hi, tlo = 0, thi = 0;
+#pragma unroll
+    for (int w = 0; w < kGuWaves; ++w) {
+        plo += w < wave ? s_cls[0][w] : 0;
+        phi += w < wave ? s_cls[1][w] : 0;
+        tlo += s_cls[0][w];
+        thi += s_cls[1][w];
+    }
+    int rank[4] = {plo & 0xFFFF, plo >> 16, phi & 0xFFFF, phi >> 16};
+    const int N[4] = {tlo & 0xFFFF, tlo >> 16, thi & 0xFFFF, thi >> 16};
+    // classes in order 3, 2, 1, 0: items and cost before each class
+    int pos0[4], cost0[4];
+    int np = 0, cp = 0;
+#pragma unroll
+    for (int c = 3; c >= 0; --c) {
+        pos0[c] = np;
+        cost0[c] = cp;
+        np += N[c];
+        cp += N[c] * gu_unit_cost(c + 1);
+    }
+    const long long den = 2LL * max(cp, 1);
+    int before = 0, mine = 0;
+    int pos[kGuPer];
+#pragma unroll
+    for (int r = 0; r < kGuPer; ++r) {
+        pos[r] = -1;
+        const int c = cls[r];
+        if (c >= 0) {
+            const int k = c == 0 ? rank[0]++ : c == 1 ? rank[1]++ : c == 2 ? rank[2]++ : rank[3]++;
+            const int cost = gu_unit_cost(c + 1);
+            const int pre = (c == 0 ? cost0[0] : c == 1 ? cost0[1] : c == 2 ? cost0[2] : cost0[3]) +
+                            k * cost;
+            const int run = (int)((long long)(2 * pre + cost) * Q / den);
+            before += run < q;
+            if (run == q) {
+                ++mine;
+                pos[r] = (c == 0 ? pos0[0] : c == 1 ? pos0[1] : c == 2 ? pos0[2] : pos0[3]) + k;
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        before += __shfl_xor(before, o, 64);
+        mine += __shfl_xor(mine, o, 64);
+    }
+    if (lane == 0) {
+        s_cnt[0][wave] = before;
+        s_cnt[1][wave] = mine;
+    }
+    __syncthreads();
+    int first = 0, n_run = 0;
+#pragma unroll
+    for (int w = 0; w < kGuWaves; ++w) {
+        first += s_cnt[0][w];
+        n_run += s_cnt[1][w];
+    }
+#pragma unroll
+    for (int r = 0; r < kGuPer; ++r)
+        if (pos[r] >= 0 && pos[r] - first < kGuRunMax) s_items[pos[r] - first] = tid * R + r;
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(min(n_run, kGuRunMax));
+}
+
 // kSB4: every row has a multiple of 8 groups (K % 512 == 0), so one 16-byte
 // load brings a lane the scales (or biases) of four consecutive chunks; they
 // are loaded once per four chunks instead of once per chunk.
@@ -772,7 +895,7 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     const int G = gridDim.x, g = blockIdx.x;
     const int K = a.d, Nw = a.I;
     const int n_tiles = *a.n_tiles;
-    const int sh_items = (a.T + kMT - 1) / kMT;
+    const int sh_items = (a.T + kGuShRows - 1) / kGuShRows;
     const int n_items = n_tiles + sh_items;
     const int NL = ((K + kKC - 1) / kKC + kStages - 1) / kStages * kStages;  // chunks per unit
     const bool pair_sb = (K / kGroup) % 2 == 0;  // scale/bias pairs are 4-byte aligned
@@ -802,16 +925,40 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
         __shared__ int s_wtot[kGuWaves];
         down_schedule(a, s_wtot);
     }
+    // Grouped schedule: the work groups on one XCD (g % 8) form groups of
+    // n_cb; a group takes a cost-balanced contiguous run of items and its
+    // members one column block each, so the column blocks of an item run at
+    // the same time on one XCD (sharing its L2 for the gathered activation
+    // rows) and every group carries about the same work.  Otherwise (a grid
+    // that does not split so): the round-robin list below.
+    const int gpx = (G / 8) / n_cb;  // groups per XCD
+    const bool grouped = kGuGrouped && G % 8 == 0 && gpx > 0 &&
+                         (long long)n_items <= (long long)kGuRunMax * 8 * gpx / 4;
+    __shared__ int s_items[kGuRunMax];
+    int i_next = 0, i_end = 0, my_cb = 0;
+    if (grouped) {
+        const int x = g % 8, j = g / 8;
+        if (j >= gpx * n_cb) return;  // uniform: no group for this work group
+        my_cb = j % n_cb;
+        i_end = item_run(a, n_tiles, n_items, 8 * gpx, x * gpx + j / n_cb, s_items);
+    }
     int u_next = g;
     while (true) {
         // ---- descriptors of up to kBatch units ----
         __syncthreads();  // the previous batch is done with s_unit / s_src / s_dst
         int nb = 0;
-        while (nb < kBatch && u_next < n_units) {
-            const int blk = u_next / (8 * n_cb), r = u_next - blk * 8 * n_cb;
-            const int cb = r >> 3, item = blk * 8 + (r & 7);
-            u_next += G;
-            if (item >= n_items) continue;
+        while (nb < kBatch && (grouped ? i_next < i_end : u_next < n_units)) {
+            int cb, item;
+            if (grouped) {
+                cb = my_cb;
+                item = s_items[i_next++];
+            } else {
+                const int blk = u_next / (8 * n_cb), r = u_next - blk * 8 * n_cb;
+                cb = r >> 3;
+                item = blk * 8 + (r & 7);
+                u_next += G;
+                if (item >= n_items) continue;
+            }
             const int bi = nb++;
             int e = 0, row0, M, shared = 0;
             if (item < n_tiles) {
@@ -820,8 +967,8 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 M = min(kMT, a.offsets[e + 1] - row0);
             } else {
                 shared = 1;
-                row0 = (item - n_tiles) * kMT;
-                M = min(kMT, a.T - row0);
+                row0 = (item - n_tiles) * kGuShRows;
+                M = min(kGuShRows, a.T - row0);
             }
             if (tid == 0) s_unit[bi] = UnitDesc{e, row0, M, cb, shared};
             if (tid < kMT) {
@@ -1156,7 +1303,7 @@ static hipError_t launch_gate_up(const PrefillArgs& a_in, hipStream_t s) {
     PrefillArgs a = a_in;
     if (!down_is_resident(a)) a.dn_pre = nullptr;
     const int n_cb = (a.I + kGuCols - 1) / kGuCols;
-    const int sh_items = (a.T + kMT - 1) / kMT;
+    const int sh_items = (a.T + kGuShRows - 1) / kGuShRows;
     const int max_units = (a.tile_bound + sh_items + 7) / 8 * 8 * n_cb;
     int grid = device_cus();
     if (grid > max_units) grid = max_units;
