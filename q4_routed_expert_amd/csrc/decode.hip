@@ -12,7 +12,8 @@
 // dependencies allow), each spread over thousands of waves so that the
 // weight loads of many waves are in flight at once:
 //   1. router partial sums (ceil(d/128) work groups, each sums 128 rows of
-//      x . W_r for every expert; skipped when the logits are given) and, in
+//      x . W_r for every expert, a whole row per load instruction; skipped
+//      when the logits are given) and, in
 //      the same launch, the shared expert's gate/up rows, which need no
 //      routing;
 //   2. every work group adds the partial sums in a fixed order (+ bias) and
@@ -31,19 +32,20 @@
 namespace q4moe {
 
 constexpr int kRouterRows = 128;  // rows of W_r per router work group (DecodeWs sizes partial by it)
-constexpr int kRouterQuarters = 4;
-constexpr int kRouterThreadRows = kRouterRows / kRouterQuarters;
+constexpr int kRouterWaves = 16;
+constexpr int kRouterWaveRows = kRouterRows / kRouterWaves;
 constexpr int kDecRows = 16;  // gate/up rows per 1024-thread work group, one wave each
+constexpr int kDownWaves = 8;  // down outputs per work group, one wave each
 
 static_assert(kRouterRows == MOE_DECODE_ROUTER_ROWS, "router partial rows");
-static_assert(kRouterQuarters * kMaxExperts == 1024, "router work group shape");
+static_assert(kRouterWaves * 64 == 1024 && 4 * 64 == kMaxExperts, "router work group shape");
 
 // One wave: h[slot][j] = bf16(SiLU(W_gate[e] x)_j * (W_up[e] x)_j) for expert
 // e (or the shared expert); lane covers 32 consecutive k of each 2048-wide
 // pass (half a quantisation group).  Weights are the bf16 values
 // bf16(q * s + b), as in the grouped GEMM, dotted with bf16 x in fp32.
-__device__ __forceinline__ void gate_up_row(const DecodeArgs& a, int slot, bool shared, int e,
-                                            int j, int lane) {
+__device__ __forceinline__ void gate_up_row(const DecodeArgs& a, const uint16_t* s_x, int slot,
+                                            bool shared, int e, int j, int lane) {
     const int d = a.d;
     const size_t row = shared ? (size_t)j : (size_t)e * a.I + j;
     const uint32_t* gq = (shared ? a.sh_gate.q : a.gate.q) + row * (d / 8);
@@ -62,7 +64,7 @@ __device__ __forceinline__ void gate_up_row(const DecodeArgs& a, int slot, bool 
         const float u_s = dq_scale(us[kk / kGroup]), u_b = bf16_to_f32(ub[kk / kGroup]);
         u32x4 xv[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) xv[p] = ((const u32x4*)(a.x + kk))[p];
+        for (int p = 0; p < 4; ++p) xv[p] = ((const u32x4*)(s_x + kk))[p];
         float gp = 0.0f, up = 0.0f;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -76,39 +78,74 @@ __device__ __forceinline__ void gate_up_row(const DecodeArgs& a, int slot, bool 
     if (lane == 0) a.h[(size_t)slot * a.I + j] = f32_to_bf16(silu(g) * u);
 }
 
+// Copies x (d bf16, 16-byte pieces) into the work group's LDS: every wave of
+// the group then reads its x operand from there instead of from L2.
+__device__ __forceinline__ void stage_x(const DecodeArgs& a, uint16_t* s_x, int tid, int n_threads) {
+    for (int i = tid; i < a.d / 8; i += n_threads)
+        ((u32x4*)s_x)[i] = ((const u32x4*)a.x)[i];
+}
+
 // Work groups [0, n_part): partial[g][e] = sum of x[r] W_r[r][e] over the 128
-// rows r of group g (four quarters of 32 rows summed in parallel, then the
-// quarters in order).  Work groups from n_part on: the shared expert's
+// rows r of group g.  Wave w takes rows 8w .. 8w + 7 of the group, each lane
+// four consecutive experts: one 16-byte load per row and lane, so one load
+// instruction reads a whole 1 KB row of W_r (E = 256); x[r] is wave-uniform
+// and comes through the scalar cache.  The sixteen waves' sums are then added
+// in wave order through LDS.  Work groups from n_part on: the shared expert's
 // gate/up rows, one per wave.
+template <bool VEC>
 __global__ __launch_bounds__(1024) void decode_router_shared_kernel(const DecodeArgs a,
                                                                     int n_part) {
-    __shared__ float s_q[kRouterQuarters][kMaxExperts];
+    __shared__ float s_q[kRouterWaves][kMaxExperts];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[MOE_MAX_D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if ((int)blockIdx.x >= n_part) {
+    if ((int)blockIdx.x >= n_part) {  // uniform per work group
+        stage_x(a, s_x, tid, 1024);
+        __syncthreads();
         const int j = ((int)blockIdx.x - n_part) * kDecRows + wave;
-        if (j < a.I) gate_up_row(a, a.k, true, 0, j, lane);
+        if (j < a.I) gate_up_row(a, s_x, a.k, true, 0, j, lane);
         return;
     }
     if (a.logits_in) return;  // uniform
     const int g = blockIdx.x, E = a.E, d = a.d;
-    const int e = tid & (kMaxExperts - 1), q = tid / kMaxExperts;
-    const int r0 = g * kRouterRows + q * kRouterThreadRows;
-    const int ee = e < E ? e : 0;  // clamped, always valid
-    float w[kRouterThreadRows], xv[kRouterThreadRows];
+    const int e0 = 4 * lane;
+    // first row of this wave, made explicitly wave-uniform for the scalar loads of x
+    const int r0 = __builtin_amdgcn_readfirstlane(g * kRouterRows + wave * kRouterWaveRows);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 w[kRouterWaveRows];
 #pragma unroll
-    for (int r = 0; r < kRouterThreadRows; ++r) {
-        const int rr = r0 + r < d ? r0 + r : 0;
-        w[r] = a.w_router[(size_t)rr * E + ee];
-        xv[r] = bf16_to_f32(a.x[rr]);
+    for (int r = 0; r < kRouterWaveRows; ++r) {
+        const uint32_t rr = (uint32_t)(r0 + r < d ? r0 + r : 0);  // clamped, always valid
+        if constexpr (VEC) {
+            const uint32_t ee = (uint32_t)(e0 < E ? e0 : 0);
+            w[r] = *(const u32x4*)(a.w_router + (rr * (uint32_t)E + ee));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t ee = (uint32_t)(e0 + i < E ? e0 + i : 0);
+                w[r][i] = __float_as_uint(a.w_router[rr * (uint32_t)E + ee]);
+            }
+        }
     }
-    float acc = 0.0f;
+    // x[r0 .. r0 + 7]: one uniform 16-byte load (r0 is a multiple of 8 and d of 64)
+    const bool r_ok = r0 < d;
+    const u32x4 xq = *(const u32x4*)(a.x + (r_ok ? r0 : 0));
 #pragma unroll
-    for (int r = 0; r < kRouterThreadRows; ++r)
-        acc = r0 + r < d ? __builtin_fmaf(xv[r], w[r], acc) : acc;
-    s_q[q][e] = acc;
+    for (int r = 0; r < kRouterWaveRows; ++r) {
+        const uint32_t xw = xq[r >> 1];
+        const float xv = r_ok ? __uint_as_float((r & 1) ? (xw & 0xffff0000u) : (xw << 16)) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(xv, __uint_as_float(w[r][i]), acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (e0 + i < kMaxExperts) s_q[wave][e0 + i] = acc[i];
     __syncthreads();
-    if (tid < E)
-        a.partial[(size_t)g * E + tid] = ((s_q[0][tid] + s_q[1][tid]) + s_q[2][tid]) + s_q[3][tid];
+    if (tid < E) {
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kRouterWaves; ++q) v += s_q[q][tid];
+        a.partial[(size_t)g * E + tid] = v;
+    }
 }
 
 // Logits (partial sums added in order, + bias; or the given logits), top-k,
@@ -118,9 +155,11 @@ __global__ __launch_bounds__(1024) void decode_router_shared_kernel(const Decode
 __global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeArgs a, int n_part) {
     __shared__ float s_logits[kMaxExperts];
     __shared__ int s_sel[kMaxTopK];
+    __shared__ __attribute__((aligned(16))) uint16_t s_x[MOE_MAX_D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, E = a.E;
     const int slot = blockIdx.y;
     const bool first = blockIdx.x == 0 && slot == 0;
+    stage_x(a, s_x, tid, 1024);  // covered by the barrier after the logits
     if (tid < E) {
         float v;
         if (a.logits_in) {
@@ -159,18 +198,23 @@ __global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeA
     }
     __syncthreads();
     const int j = blockIdx.x * kDecRows + wave;
-    if (j < a.I) gate_up_row(a, slot, false, s_sel[slot], j, lane);
+    if (j < a.I) gate_up_row(a, s_x, slot, false, s_sel[slot], j, lane);
 }
 
 // One wave per output n; lane covers 8 consecutive intermediate k (one code
 // word) of each 512-wide pass, for every slot.  All slots' loads are issued
 // before the arithmetic; the combine then adds w_s * P_s in slot order and
 // the shared expert last.
-__global__ __launch_bounds__(256) void decode_down_kernel(const DecodeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (n >= a.d) return;
+__global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(const DecodeArgs a) {
+    // h of all k + 1 experts, staged once per work group
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[(kMaxTopK + 1) * MOE_MAX_INTER];
+    const int tid = threadIdx.x, lane = tid & 63;
     const int I = a.I, k = a.k, d = a.d;
+    for (int i = tid; i < (k + 1) * I / 8; i += 64 * kDownWaves)
+        ((u32x4*)s_h)[i] = ((const u32x4*)a.h)[i];
+    __syncthreads();
+    const int n = blockIdx.x * kDownWaves + (tid >> 6);
+    if (n >= d) return;
     float part[kMaxTopK + 1];
 #pragma unroll
     for (int s = 0; s <= kMaxTopK; ++s) part[s] = 0.0f;
@@ -189,7 +233,7 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const DecodeArgs a) {
             q[s] = D.q[row * (I / 8) + jj / 8];
             sc[s] = D.scale[row * (I / kGroup) + jj / kGroup];
             bi[s] = D.bias[row * (I / kGroup) + jj / kGroup];
-            hv[s] = *(const u32x4*)(a.h + (size_t)ss * I + jj);
+            hv[s] = *(const u32x4*)(s_h + ss * I + jj);
         }
 #pragma unroll
         for (int s = 0; s <= kMaxTopK; ++s) {
@@ -212,8 +256,12 @@ __global__ __launch_bounds__(256) void decode_down_kernel(const DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     const int n_part = (a.d + kRouterRows - 1) / kRouterRows;
     const int n_rows = (a.I + kDecRows - 1) / kDecRows;
-    hipLaunchKernelGGL(decode_router_shared_kernel, dim3(n_part + n_rows), dim3(1024), 0, s, a,
-                       n_part);
+    if (a.E % 4 == 0)
+        hipLaunchKernelGGL(decode_router_shared_kernel<true>, dim3(n_part + n_rows), dim3(1024), 0,
+                           s, a, n_part);
+    else
+        hipLaunchKernelGGL(decode_router_shared_kernel<false>, dim3(n_part + n_rows), dim3(1024),
+                           0, s, a, n_part);
     trace_point(s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -221,7 +269,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     trace_point(s);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(decode_down_kernel, dim3((a.d + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_down_kernel, dim3((a.d + kDownWaves - 1) / kDownWaves),
+                       dim3(64 * kDownWaves), 0, s, a);
     trace_point(s);
     return hipGetLastError();
 }

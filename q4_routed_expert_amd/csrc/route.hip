@@ -204,6 +204,13 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(
     __shared__ int s_cnt[kMaxExperts], s_before[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1], s_b32[kMaxExperts + 1], s_b128[kMaxExperts + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = blockIdx.x;
+    // this block's selections, loaded first so that their round trip overlaps
+    // the count-table reads below
+    const int t = g * kRouteBlock + tid;
+    const bool valid = t < T;
+    int ex[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) ex[s] = (valid && s < k) ? idx[(size_t)t * k + s] : 0;
 
     // 1. totals and earlier-block counts
     if (tid < E) {
@@ -263,17 +270,9 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(
         }
     }
     // 3a. this block's token masks
-    const int t = g * kRouteBlock + tid;
-    const bool valid = t < T;
-    int ex[kMaxTopK];
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        ex[s] = 0;
-        if (valid && s < k) {
-            ex[s] = idx[(size_t)t * k + s];
-            atomicOr(&mask[wave][ex[s]], 1ull << lane);
-        }
-    }
+    for (int s = 0; s < kMaxTopK; ++s)
+        if (valid && s < k) atomicOr(&mask[wave][ex[s]], 1ull << lane);
     __syncthreads();
     if (g == 0 && tid < E) {  // 2b. counts, offsets and both maps
         const int c = s_cnt[tid], o = s_off[tid];

@@ -206,6 +206,7 @@ EDGE = [
     (70, 256, 128, 8, 8, False, 4),       # k = E: every expert selected
     (100, 256, 128, 256, 8, False, 5),    # most experts empty
     (129, 256, 64, 16, 1, True, 6),       # k = 1, one row past a tile
+    (90, 320, 128, 37, 5, True, 7),       # E not a multiple of 4 (router column loads), d = 5 x 64
 ]
 
 
@@ -261,13 +262,20 @@ def test_routing_at_the_token_limit(dev):
 
 def test_small_decode_shapes(dev):
     rng = np.random.default_rng(10)
-    for d, inter, E, k, bias in ((576, 192, 40, 3, True), (256, 128, 8, 8, False)):
+    for d, inter, E, k, bias in ((576, 192, 40, 3, True), (256, 128, 8, 8, False),
+                                 (320, 128, 37, 5, True)):
         L = random_layer(rng, d, inter, E, k, router_bias=bias)
         layer = q4.DeviceLayer.from_host(L, dev)
         ws = q4.workspace(layer, 1, dev)
         x = random_x(rng, 1, d)
         ref = oracle.layer(L, x)
         r = q4.DeviceRouting(1, E, k, dev)
+        q4.decode(layer, xdev(x, dev), ws, routing=r)  # the decode path's own router
+        torch.cuda.synchronize()
+        lrms = float(np.sqrt(np.mean(ref["logits"].astype(np.float64) ** 2)))
+        lerr = float(np.abs(r.logits.cpu().numpy() - ref["logits"]).max()) / lrms
+        log(f"decode d={d} E={E}: logits err/rms={lerr:.3e}")
+        assert lerr <= LOGIT_TOL
         r.logits.copy_(torch.from_numpy(ref["logits"]))
         y = q4.decode(layer, xdev(x, dev), ws, routing=r, logits_in=True)
         torch.cuda.synchronize()
