@@ -5,7 +5,11 @@ One step = one prefill layer call on the T=2048 chunk (moe_route + moe_prefill:
 router logits, top-8, histogram/scan/scatter/block maps, gate/up grouped GEMM
 with SiLU*up, routed down GEMM, shared down + fixed-order combine), inputs
 resident in HBM, two distinct weight sets alternated so the weights stream
-from HBM.  After the timed prefill steps the batch-1 decode layer is measured
+from HBM; only two events bracket the timed steps, and the per-kernel split
+comes from separate steps with an event after every kernel.  The same steps
+are also captured in a HIP graph (two layer calls, one per weight set) and
+replayed as a cross-check (`graph`: time and bit-equality with the eager
+output).  After the timed prefill steps the batch-1 decode layer is measured
 on 40 distinct layers cycled for `--decode-steps` steps (one moe_decode call
 per layer, every call on one stream), and the CPU oracle is timed on a bounded
 sample of the prefill workload.  Prints one JSON line.
@@ -178,27 +182,34 @@ def bench_prefill(args, q4, torch, ev, stream):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # timed steps: only two events around the whole loop
     K = args.steps
-    ev_r = [ev.make(4) for _ in range(K)]
-    ev_p = [ev.make(4) for _ in range(K)]
     t = ev.make(2)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     ev.record(t[0], stream)
     for i in range(K):
-        step(args.warmup + i, ev_r[i], ev_p[i])
+        step(args.warmup + i)
     ev.record(t[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = ev.ms(t[0], t[1]) / K
+    # per-kernel split from separate steps with an event after every kernel
+    # (each event adds a little to the kernel it follows)
+    Kt = min(K, 20)
+    ev_r = [ev.make(4) for _ in range(Kt)]
+    ev_p = [ev.make(4) for _ in range(Kt)]
+    for i in range(Kt):
+        step(args.warmup + K + i, ev_r[i], ev_p[i])
+    torch.cuda.synchronize()
     names_r = ["router_logits", "topk_histogram", "route_scatter"]
     names_p = ["gate_up", "down", "combine"]
     per = {n: 0.0 for n in names_r + names_p}
-    for i in range(K):
+    for i in range(Kt):
         for j, n in enumerate(names_r):
-            per[n] += ev.ms(ev_r[i][j], ev_r[i][j + 1]) / K
+            per[n] += ev.ms(ev_r[i][j], ev_r[i][j + 1]) / Kt
         for j, n in enumerate(names_p):
-            per[n] += ev.ms(ev_p[i][j], ev_p[i][j + 1]) / K
+            per[n] += ev.ms(ev_p[i][j], ev_p[i][j + 1]) / Kt
     counts = r.counts.cpu().numpy()
     work = prefill_work(w.T, w.d, w.inter, w.n_experts, w.top_k, counts)
     sec = ms_step / 1e3
@@ -211,6 +222,35 @@ def bench_prefill(args, q4, torch, ev, stream):
         "tok_s": w.T / sec, "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "gbps": work["bytes"] / sec / 1e9, "work": work, "kernel_us": {n: v * 1e3 for n, v in per.items()},
     }
+    # two layer steps (route + prefill on each weight set) captured once in a
+    # HIP graph and replayed; the output must equal the eager output
+    if not args.no_graph:
+        for i in range(2):
+            step(i)
+        torch.cuda.synchronize()
+        y_eager = y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(2):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(y, y_eager))
+        reps = max(1, K // 2)
+        t2 = ev.make(2)
+        gs = int(torch.cuda.current_stream().cuda_stream)
+        ev.record(t2[0], gs)
+        for _ in range(reps):
+            g.replay()
+        ev.record(t2[1], gs)
+        torch.cuda.synchronize()
+        us_g = ev.ms(t2[0], t2[1]) * 1e3 / (2 * reps)
+        out["graph"] = {"us_per_layer": us_g, "tok_s": w.T / (us_g * 1e-6),
+                        "mfma_frac": work["flops"] / (us_g * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                        "replays": reps, "layers_per_replay": 2, "matches_eager": same}
+        log(f"prefill graph: {us_g:.1f} us/layer, output equal to eager: {same}")
+        del g
     gu_sec = per["gate_up"] / 1e3
     out["roofline"] = roofline(work["gate_up"]["flops"], work["gate_up"]["bytes"], gu_sec)
     out["roofline"]["kernel"] = "gate_up_kernel (grouped gate/up GEMM + SiLU*up)"
@@ -305,6 +345,69 @@ def bench_decode(args, q4, torch, ev, stream):
     return out
 
 
+def bench_sweep(args, q4, torch, ev, stream):
+    """Prefill layer time over chunk sizes T (balanced and skewed router), the
+    small-T verify shapes (T = 1..8 through the same prefill path) included.
+    Weights: two sets alternated, as in the headline; x: the first T rows of one
+    seeded draw; the skewed rows add the skewed workload's router bias."""
+    from workloads import WORKLOADS, make_layer, skew_bias
+    Ts = [int(t) for t in args.sweep.split(",")]
+    base = WORKLOADS["prefill2048"]
+    w = dataclasses.replace(base, T=max(Ts))
+    log(f"sweep: generating two weight sets and x for T up to {w.T}")
+    L0, x = make_layer(w)
+    L1, _ = make_layer(dataclasses.replace(w, seed=w.seed + 100))
+    bias = skew_bias(np.random.Generator(np.random.PCG64(w.seed + 200)), w.n_experts)
+    dev = torch.device("cuda:0")
+    sets = {False: [q4.DeviceLayer.from_host(L, dev) for L in (L0, L1)],
+            True: [q4.DeviceLayer.from_host(dict(L, router_bias=bias), dev) for L in (L0, L1)]}
+    del L0, L1
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = q4.workspace(sets[False][0], w.T, dev)
+    rows = []
+    for skew in (False, True):
+        for T in Ts:
+            if skew and T < 256:
+                continue
+            r = q4.DeviceRouting(T, w.n_experts, w.top_k, dev)
+            y = torch.empty((T, w.d), dtype=torch.bfloat16, device=dev)
+            xs = xd[:T]
+
+            def step(i):
+                q4.route(sets[skew][i % 2], xs, routing=r)
+                q4.prefill(sets[skew][i % 2], xs, r, ws, y)
+
+            for i in range(3):
+                step(i)
+            torch.cuda.synchronize()
+            n = max(4, min(args.steps, 20))
+            t = ev.make(2)
+            ev.record(t[0], stream)
+            for i in range(n):
+                step(i)
+            ev.record(t[1], stream)
+            torch.cuda.synchronize()
+            us = ev.ms(t[0], t[1]) * 1e3 / n
+            counts = r.counts.cpu().numpy()
+            work = prefill_work(T, w.d, w.inter, w.n_experts, w.top_k, counts)
+            sec = us * 1e-6
+            row = {"T": T, "skew": skew, "us_per_layer": round(us, 2), "tok_s": round(T / sec, 1),
+                   "tflops": round(work["flops"] / sec / 1e12, 2),
+                   "mfma_frac": round(work["flops"] / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "gbps": round(work["bytes"] / sec / 1e9, 1),
+                   "hbm_frac": round(work["bytes"] / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                   "touched_experts": work["touched_experts"],
+                   "weight_bytes_per_token": round((work["bytes"] - 4 * T * w.d) / T, 1)}
+            rows.append(row)
+            log(f"sweep T={T} skew={skew}: {us:.1f} us/layer, {row['tok_s']:.0f} tok/s, "
+                f"MFMA {row['mfma_frac']:.3f}, HBM {row['hbm_frac']:.3f}, "
+                f"{row['touched_experts']} experts touched")
+            del r, y
+    del sets, ws
+    torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(n_tokens):
     import oracle
     from workloads import WORKLOADS, make_layer
@@ -333,6 +436,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--sweep", default=None, metavar="T1,T2,...",
+                    help="only the prefill sweep over these chunk sizes (balanced and skewed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB copy (for HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -351,14 +456,24 @@ def main():
     stream = int(torch.cuda.current_stream().cuda_stream)
     if args.copy_calibration:
         copy_calibration(torch)
+    if args.sweep:
+        rows = bench_sweep(args, q4, torch, ev, stream)
+        ev.close()
+        print(json.dumps({"metric": "prefill MoE-layer us/layer over chunk sizes T", "unit": "us",
+                          "n_gpus": 1, "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": "routed-MoE FFN layer, d=2048, I=512, E=256, "
+                                                 "top-8 + 1 shared, Q4 group-64, 2 weight sets"},
+                          "sweep": rows}), flush=True)
+        return
     pre = bench_prefill(args, q4, torch, ev, stream)
     dec = None if args.no_decode else bench_decode(args, q4, torch, ev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
     ev.close()
     w = pre["workload"]
+    ms_step = pre["ms_per_step"]
     line = {
-        "metric": METRIC, "value": round(pre["tok_s"], 1), "unit": "tok/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 4),
+        "metric": METRIC, "value": round(w.T / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"routed-MoE FFN layer, prefill chunk T={w.T}, d={w.d}, "
@@ -366,14 +481,19 @@ def main():
                                f"Q4 group-64 weights (bf16 scale/bias), 2 weight sets alternated",
                    "T": w.T, "d": w.d, "inter": w.inter, "n_experts": w.n_experts,
                    "top_k": w.top_k, "seed": w.seed},
-        "us_per_layer": round(pre["ms_per_step"] * 1e3, 2),
-        "tflops": round(pre["tflops"], 2), "mfma_frac": round(pre["mfma_frac"], 4),
-        "gbps": round(pre["gbps"], 1), "hbm_frac": round(pre["gbps"] / PEAK_HBM_GBPS, 4),
+        "us_per_layer": round(ms_step * 1e3, 2),
+        "tflops": round(pre["work"]["flops"] / (ms_step * 1e-3) / 1e12, 2),
+        "mfma_frac": round(pre["work"]["flops"] / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gbps": round(pre["work"]["bytes"] / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(pre["work"]["bytes"] / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kernel_us": {n: round(v, 2) for n, v in pre["kernel_us"].items()},
         "algorithmic": {"flops": pre["work"]["flops"], "bytes": pre["work"]["bytes"],
                         "touched_experts": pre["work"]["touched_experts"]},
         "roofline": pre["roofline"],
     }
+    if "graph" in pre:
+        line["graph"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                         for k, v in pre["graph"].items()}
     if dec is not None:
         line["decode"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in dec.items()
                           if k not in ("roofline", "graph", "kernel_us")}

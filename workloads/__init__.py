@@ -121,12 +121,15 @@ def make_layer(w: Workload, layer: int = 0):
     L["w_router"] = (rng.standard_normal((w.d, w.n_experts), dtype=np.float32)
                      * np.float32(1.0 / np.sqrt(w.d))).astype(np.float32)
     L.update(_experts(rng, w.n_experts, w.d, w.inter))
-    L["router_bias"] = None
-    if w.skew:
-        rank = rng.permutation(w.n_experts).astype(np.float64) + 1.0
-        # b_e = 3 * ln(1 / rank_e^1.1): a fixed per-expert preference, Zipf-like load
-        L["router_bias"] = (3.0 * np.log(1.0 / rank ** 1.1)).astype(np.float32)
+    L["router_bias"] = skew_bias(rng, w.n_experts) if w.skew else None
     return L, x
+
+
+def skew_bias(rng: np.random.Generator, E: int) -> np.ndarray:
+    """The skewed workload's router bias: b_e = 3 * ln(1 / rank_e^1.1) with rank a
+    seeded permutation of 1..E (a fixed per-expert preference, Zipf-like load)."""
+    rank = rng.permutation(E).astype(np.float64) + 1.0
+    return (3.0 * np.log(1.0 / rank ** 1.1)).astype(np.float32)
 
 
 def decode_inputs(w: Workload, n_steps: int | None = None):
