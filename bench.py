@@ -333,6 +333,55 @@ def bench_decode(args, q4, torch, ev, stream):
         log(f"decode graph: {us_g:.2f} us/layer ({out['graph']['gbps']:.0f} GB/s), "
             f"output equal to eager: {same}")
         del g
+    # the few-token decode shape: moe_decode_tokens on T tokens per call
+    out["tokens"] = []
+    for T in (2, 4, 8):
+        if args.decode_steps < 4:
+            break
+        xt = torch.from_numpy(decode_inputs(w, 8 * 32).view(np.int16)).to(dev).view(torch.bfloat16)
+        n_st = max(2, n_steps // 4)
+        yT = torch.empty((T, w.d), dtype=torch.bfloat16, device=dev)
+        for li in range(n_layers):
+            q4.decode_tokens(layers[li], xt[0:T], ws, yT)
+        torch.cuda.synchronize()
+        tT = ev.make(2)
+        ev.record(tT[0], stream)
+        for st in range(n_st):
+            x0 = (st * T) % (xt.shape[0] - T + 1)
+            for li in range(n_layers):
+                q4.decode_tokens(layers[li], xt[x0:x0 + T], ws, yT)
+        ev.record(tT[1], stream)
+        torch.cuda.synchronize()
+        usT = ev.ms(tT[0], tT[1]) * 1e3 / (n_st * n_layers)
+        # per-kernel split over one more pass of the layers
+        evT = [ev.make(4) for _ in range(n_layers)]
+        for li in range(n_layers):
+            lib.moe_trace_events(C.cast(evT[li], C.c_void_p), 4)
+            q4.decode_tokens(layers[li], xt[0:T], ws, yT)
+            lib.moe_trace_events(None, 0)
+        torch.cuda.synchronize()
+        perT = [sum(ev.ms(evT[li][j], evT[li][j + 1]) for li in range(n_layers)) * 1e3 / n_layers
+                for j in range(3)]
+        # distinct experts the T tokens select, over one pass of the layers
+        rT = q4.DeviceRouting(T, w.n_experts, w.top_k, dev)
+        uni = []
+        for li in range(n_layers):
+            q4.decode_tokens(layers[li], xt[0:T], ws, yT, routing=rT)
+            uni.append(len(np.unique(rT.topk_idx.cpu().numpy())))
+        n_uni = float(np.mean(uni))
+        per_expert = expert_bytes // (w.top_k + 1)
+        bytesT = (n_uni + 1) * per_expert
+        rec = {"T": T, "us_per_layer": round(usT, 3), "us_per_token": round(usT / T, 3),
+               "distinct_experts": round(n_uni, 2), "expert_bytes_per_layer": int(bytesT),
+               "gbps": round(bytesT / (usT * 1e-6) / 1e9, 1),
+               "hbm_frac": round(bytesT / (usT * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+               "bytes_per_token": int(bytesT / T),
+               "kernel_us": {n: round(v, 3) for n, v in zip(names, perT)}}
+        out["tokens"].append(rec)
+        log(f"decode T={T}: {usT:.2f} us/layer ({usT / T:.2f} us/token), {n_uni:.1f} distinct "
+            f"experts, {rec['gbps']:.0f} GB/s on their bytes, per kernel (us): " +
+            ", ".join(f"{n}={v:.2f}" for n, v in zip(names, perT)))
+        del rT
     ex_bytes = expert_bytes
     k_sec = sum(per.values()) / 1e6
     out["roofline"] = {"bound": "hbm", "achieved": round(ex_bytes / k_sec / 1e9, 1),
@@ -496,11 +545,12 @@ def main():
                          for k, v in pre["graph"].items()}
     if dec is not None:
         line["decode"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in dec.items()
-                          if k not in ("roofline", "graph", "kernel_us")}
+                          if k not in ("roofline", "graph", "kernel_us", "tokens")}
         line["decode"]["kernel_us"] = {n: round(v, 3) for n, v in dec["kernel_us"].items()}
         if "graph" in dec:
             line["decode"]["graph"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                        for k, v in dec["graph"].items()}
+        line["decode"]["tokens"] = dec["tokens"]
         line["roofline_decode"] = dec["roofline"]
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -85,8 +85,12 @@ enum {
 #define MOE_ROUTE_BLOCK 256
 
 /* moe_decode sums the router logits in partial sums over this many rows of
-   W_r (the workspace holds ceil(d / MOE_DECODE_ROUTER_ROWS) x E of them). */
+   W_r (the workspace holds ceil(d / MOE_DECODE_ROUTER_ROWS) x E of them per
+   token). */
 #define MOE_DECODE_ROUTER_ROWS 128
+
+/* Most tokens one moe_decode_tokens call takes. */
+#define MOE_MAX_DECODE_TOKENS 8
 
 /* moe_route flag: start from the logits already in routing->logits instead of
    computing them (used to route from given fp32 logits). */
@@ -146,8 +150,9 @@ typedef struct {
 /* Entries needed in block_map / tile_map for T tokens (pairs of int32). */
 int32_t moe_block_map_capacity(int32_t T, int32_t top_k, int32_t n_experts, int32_t rows);
 
-/* Bytes of device workspace moe_prefill (T tokens) and moe_decode (T = 1)
-   need for this layer shape: the gate/up activations h (bf16), the shared
+/* Bytes of device workspace moe_prefill (T tokens), moe_decode and
+   moe_decode_tokens (up to MOE_MAX_DECODE_TOKENS tokens, whatever T) need for
+   this layer shape: the gate/up activations h (bf16), the shared
    expert's activations, the routed experts' fp16 outputs and the shared
    expert's fp32 outputs before the combine, and the decode path's router
    partial sums.  0 on invalid arguments.  The
@@ -183,6 +188,23 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
 int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_routing* r,
                void* ws, size_t ws_bytes, uint16_t* y, void* stream);
 
+/* The decode layer for a few tokens at once, 1 <= T <= MOE_MAX_DECODE_TOKENS
+   (the small-batch decode or draft-verify shape, where the tokens' rows route
+   to different experts and the bytes read grow with the experts they select):
+   the same three kernels as moe_decode, with every W_r row and every shared
+   expert weight read and dequantised once for all T tokens, and every token's
+   routed slots as separate work groups.  Per token the arithmetic is exactly
+   moe_decode's, so moe_decode_tokens(T) gives each token's moe_decode result
+   bit for bit.  x, y: bf16 [T][d]; r may be NULL, else r->logits [T][E],
+   r->topk_idx [T][k] and r->topk_w [T][k] are written (MOE_LOGITS_IN: the
+   logits are read).  ws must hold moe_workspace_bytes(L, 1) bytes; T outside
+   1 .. MOE_MAX_DECODE_TOKENS is MOE_EUNSUPPORTED.  ([Lily-M5] "Decode:
+   minimize bytes per token"; its closing discussion of the small-batch and
+   verification shapes.) */
+int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                      const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
+                      void* stream);
+
 /* The on-chip dequantisation the GEMMs use, exposed for testing: w_out (bf16
    [n_rows][K]) = bf16(q * scale + bias) for matrix 0 of m.  K % 64 == 0. */
 int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, void* stream);
@@ -193,8 +215,9 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
    i < n (moe_route: router logits (with MOE_LOGITS_IN: the clearing of
    the histogram), top-k + histogram, scan + scatter + maps;
    moe_prefill: gate/up, down
-   (routed and shared), combine; moe_decode: router partial sums + shared
-   gate/up, logits + top-k + routed gate/up, down + combine).  The
+   (routed and shared), combine; moe_decode and moe_decode_tokens: router
+   partial sums + shared gate/up, logits + top-k + routed gate/up, down +
+   combine).  The
    elapsed time between consecutive events is one kernel's duration.  events
    are hipEvent_t handles created and owned by the caller; pass NULL to stop. */
 void moe_trace_events(void* const* events, int32_t n);

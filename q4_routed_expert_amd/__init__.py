@@ -20,6 +20,7 @@ import torch
 from . import _abi
 
 MOE_LOGITS_IN = _abi.MOE_LOGITS_IN
+MAX_DECODE_TOKENS = _abi.MOE_MAX_DECODE_TOKENS
 BLOCK_ROWS = _abi.MOE_BLOCK_ROWS
 TILE_ROWS = _abi.MOE_TILE_ROWS
 MATS = ("gate", "up", "down", "sh_gate", "sh_up", "sh_down")
@@ -151,6 +152,20 @@ def decode(layer: DeviceLayer, x: torch.Tensor, ws: torch.Tensor, y: torch.Tenso
     rs = C.addressof(routing.struct) if routing is not None else None
     _check(_abi.lib().moe_decode(C.addressof(layer.struct), _ptr(x), flags, rs, _ptr(ws), ws.numel(),
                                  _ptr(y), _stream(stream)), "moe_decode")
+    return y
+
+
+def decode_tokens(layer: DeviceLayer, x: torch.Tensor, ws: torch.Tensor,
+                  y: torch.Tensor | None = None, routing: DeviceRouting | None = None,
+                  logits_in: bool = False, stream=None) -> torch.Tensor:
+    """The decode layer for T = x.shape[0] tokens (1 <= T <= MAX_DECODE_TOKENS)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, layer.d), dtype=torch.bfloat16, device=x.device)
+    flags = MOE_LOGITS_IN if logits_in else 0
+    rs = C.addressof(routing.struct) if routing is not None else None
+    _check(_abi.lib().moe_decode_tokens(C.addressof(layer.struct), _ptr(x), T, flags, rs, _ptr(ws),
+                                        ws.numel(), _ptr(y), _stream(stream)), "moe_decode_tokens")
     return y
 
 

@@ -12,11 +12,12 @@ MOE_BLOCK_ROWS = 32
 MOE_TILE_ROWS = 128
 MOE_ROUTE_BLOCK = 256
 MOE_DECODE_ROUTER_ROWS = 128
+MOE_MAX_DECODE_TOKENS = 8
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_D, MOE_MAX_INTER = 256, 8, 32768, 8192, 2048
 
 # every function include/q4moe.h declares
 EXPORTS = ("moe_block_map_capacity", "moe_workspace_bytes", "moe_route", "moe_prefill", "moe_trace_events",
-           "moe_decode", "moe_dequant", "moe_strerror", "moe_last_error")
+           "moe_decode", "moe_decode_tokens", "moe_dequant", "moe_strerror", "moe_last_error")
 
 
 class Q4Mat(C.Structure):
@@ -62,8 +63,9 @@ def lib():
         L.moe_route.argtypes = [vp, vp, i32, C.c_uint32, vp, vp]
         L.moe_prefill.argtypes = [vp, vp, i32, vp, vp, C.c_size_t, vp, vp]
         L.moe_decode.argtypes = [vp, vp, C.c_uint32, vp, vp, C.c_size_t, vp, vp]
+        L.moe_decode_tokens.argtypes = [vp, vp, i32, C.c_uint32, vp, vp, C.c_size_t, vp, vp]
         L.moe_dequant.argtypes = [vp, i32, i32, vp, vp]
-        for f in ("moe_route", "moe_prefill", "moe_decode", "moe_dequant"):
+        for f in ("moe_route", "moe_prefill", "moe_decode", "moe_decode_tokens", "moe_dequant"):
             getattr(L, f).restype = C.c_int
         L.moe_trace_events.argtypes = [vp, i32]
         L.moe_trace_events.restype = None

@@ -104,13 +104,14 @@ struct DecodeWs {
 DecodeWs decode_ws(const moe_layer* L) {
     DecodeWs w;
     size_t o = 0;
-    w.sel_idx = o; o += align256(sizeof(int32_t) * MOE_MAX_TOPK);
-    w.sel_w = o; o += align256(sizeof(float) * MOE_MAX_TOPK);
-    w.logits = o; o += align256(sizeof(float) * L->n_experts);
+    const size_t nt = MOE_MAX_DECODE_TOKENS;
+    w.sel_idx = o; o += align256(sizeof(int32_t) * nt * MOE_MAX_TOPK);
+    w.sel_w = o; o += align256(sizeof(float) * nt * MOE_MAX_TOPK);
+    w.logits = o; o += align256(sizeof(float) * nt * L->n_experts);
     w.partial = o;
     o += align256(sizeof(float) * (size_t)((L->d + MOE_DECODE_ROUTER_ROWS - 1) / MOE_DECODE_ROUTER_ROWS) *
-                  L->n_experts);
-    w.h = o; o += align256(sizeof(uint16_t) * (size_t)(L->top_k + 1) * L->inter);
+                  nt * L->n_experts);
+    w.h = o; o += align256(sizeof(uint16_t) * nt * (size_t)(L->top_k + 1) * L->inter);
     w.total = o;
     return w;
 }
@@ -233,9 +234,18 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
 
 int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_routing* r,
                void* ws, size_t ws_bytes, uint16_t* y, void* stream) {
+    return moe_decode_tokens(L, x, 1, flags, r, ws, ws_bytes, y, stream);
+}
+
+int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                      const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
+                      void* stream) {
     int rc;
     if ((rc = check_layer(L)) || (rc = check_ptr(y, "y")) || (rc = check_ptr(ws, "workspace")))
         return rc;
+    if (T < 1 || T > MOE_MAX_DECODE_TOKENS)
+        return fail(MOE_EUNSUPPORTED, "decode takes 1..%d tokens, not T=%d", MOE_MAX_DECODE_TOKENS,
+                    T);
     if (flags & ~MOE_LOGITS_IN) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
     const bool logits_in = flags & MOE_LOGITS_IN;
     if ((rc = check_ptr(x, "x"))) return rc;
@@ -254,6 +264,7 @@ int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_
     unsigned char* base = (unsigned char*)ws;
     q4moe::DecodeArgs a;
     a.x = x;
+    a.T = T;
     a.d = L->d;
     a.I = L->inter;
     a.E = L->n_experts;

@@ -46,22 +46,22 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
-// Decode (T = 1).
+// Decode (1 <= T <= MOE_MAX_DECODE_TOKENS tokens).
 struct DecodeArgs {
-    const uint16_t* x;
-    int d, I, E, k;
+    const uint16_t* x;   // bf16 [T][d]
+    int T, d, I, E, k;
     const float* w_router;
     const float* router_bias;
     Q4 gate, up, down, sh_gate, sh_up, sh_down;
     bool logits_in;
-    float* logits;       // [E]: written, or read when logits_in
-    int32_t* out_idx;    // [k] or NULL
-    float* out_w;        // [k] or NULL
-    float* partial;      // [ceil(d/MOE_DECODE_ROUTER_ROWS)][E] router partial sums
-    int32_t* sel_idx;    // [k]
-    float* sel_w;        // [k]
-    uint16_t* h;         // bf16 [k+1][I]
-    uint16_t* y;         // bf16 [d]
+    float* logits;       // [T][E]: written, or read when logits_in
+    int32_t* out_idx;    // [T][k] or NULL
+    float* out_w;        // [T][k] or NULL
+    float* partial;      // [ceil(d/MOE_DECODE_ROUTER_ROWS)][T][E] router partial sums
+    int32_t* sel_idx;    // [T][k]
+    float* sel_w;        // [T][k]
+    uint16_t* h;         // bf16 [T][k+1][I], slot k = the shared expert
+    uint16_t* y;         // bf16 [T][d]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 

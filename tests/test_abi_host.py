@@ -36,7 +36,7 @@ def test_header_limits_match_binding():
     text = open(HEADER).read()
     for name in ("MOE_GROUP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_TOKENS", "MOE_MAX_D",
                  "MOE_MAX_INTER", "MOE_BLOCK_ROWS", "MOE_TILE_ROWS", "MOE_ROUTE_BLOCK",
-                 "MOE_DECODE_ROUTER_ROWS", "MOE_LOGITS_IN"):
+                 "MOE_DECODE_ROUTER_ROWS", "MOE_MAX_DECODE_TOKENS", "MOE_LOGITS_IN"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m, name
         if hasattr(_abi, name):
@@ -115,6 +115,29 @@ def test_prefill_checks_workspace_size_before_launch():
     assert rc == _abi.MOE_EINVAL
 
 
+@pytest.mark.parametrize("T,code", [(0, _abi.MOE_EUNSUPPORTED), (-1, _abi.MOE_EUNSUPPORTED),
+                                    (_abi.MOE_MAX_DECODE_TOKENS + 1, _abi.MOE_EUNSUPPORTED)])
+def test_decode_tokens_rejects_token_counts_outside_its_range(T, code):
+    lib = _abi.lib()
+    L = _layer()
+    rc = lib.moe_decode_tokens(C.addressof(L), FAKE, T, 0, None, FAKE, 1 << 30, FAKE, None)
+    assert rc == code
+
+
+def test_decode_tokens_checks_workspace_and_flags_before_launch():
+    lib = _abi.lib()
+    L = _layer()
+    need = lib.moe_workspace_bytes(C.addressof(L), 1)
+    rc = lib.moe_decode_tokens(C.addressof(L), FAKE, _abi.MOE_MAX_DECODE_TOKENS, 0, None, FAKE,
+                               need - 256, FAKE, None)
+    assert rc == _abi.MOE_EWORKSPACE
+    rc = lib.moe_decode_tokens(C.addressof(L), FAKE, 4, _abi.MOE_LOGITS_IN, None, FAKE, need,
+                               FAKE, None)
+    assert rc == _abi.MOE_EINVAL
+    rc = lib.moe_decode_tokens(C.addressof(L), FAKE + 8, 4, 0, None, FAKE, need, FAKE, None)
+    assert rc == _abi.MOE_EINVAL  # misaligned x
+
+
 def test_workspace_bytes_cover_the_staged_buffers():
     lib = _abi.lib()
     for T, d, I, E, k in ((2048, 2048, 512, 256, 8), (32, 512, 128, 32, 4), (1, 2048, 512, 256, 8)):
@@ -122,7 +145,11 @@ def test_workspace_bytes_cover_the_staged_buffers():
         n = lib.moe_workspace_bytes(C.addressof(L), T)
         # h, shared h, fp16 routed outputs, fp32 shared outputs
         staged = 2 * (T * k * I + T * I + T * k * d) + 4 * T * d
-        assert staged <= n <= staged + 2 * 4 * (d // 32) * E + 64 * 1024
+        # decode region for up to MOE_MAX_DECODE_TOKENS tokens: router partial
+        # sums, logits, h of the k + 1 experts per token
+        nt = _abi.MOE_MAX_DECODE_TOKENS
+        dec = 4 * -(-d // _abi.MOE_DECODE_ROUTER_ROWS) * nt * E + 4 * nt * E + 2 * nt * (k + 1) * I
+        assert staged + dec <= n <= staged + dec + 64 * 1024
     bad = _layer(d=100)
     assert lib.moe_workspace_bytes(C.addressof(bad), 16) == 0
 

@@ -196,6 +196,58 @@ def test_decode_workload(dev):
             assert err <= Y_TOL
 
 
+def _decode_tokens_case(L, xs, dev, name):
+    """moe_decode_tokens on T tokens: every output, the logits and the routing
+    bit-equal to T single-token moe_decode calls; from the oracle's logits the
+    same experts and scores as the oracle and y within tolerance."""
+    T, E, k = xs.shape[0], L["n_experts"], L["top_k"]
+    layer = q4.DeviceLayer.from_host(L, dev)
+    ws = q4.workspace(layer, 1, dev)
+    xd = xdev(xs, dev)
+    r = q4.DeviceRouting(T, E, k, dev)
+    y = q4.decode_tokens(layer, xd, ws, routing=r)
+    torch.cuda.synchronize()
+    y_bits, l_gpu = host_bits(y), r.logits.cpu().numpy()
+    idx_gpu, w_gpu = r.topk_idx.cpu().numpy(), r.topk_w.cpu().numpy()
+    for t in range(T):
+        r1 = q4.DeviceRouting(1, E, k, dev)
+        y1 = q4.decode(layer, xd[t:t + 1], ws, routing=r1)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y1)[0], y_bits[t]), (name, t)
+        assert np.array_equal(r1.logits.cpu().numpy()[0], l_gpu[t]), (name, t)
+        assert np.array_equal(r1.topk_idx.cpu().numpy()[0], idx_gpu[t]), (name, t)
+        assert np.array_equal(r1.topk_w.cpu().numpy()[0], w_gpu[t]), (name, t)
+    ref = oracle.layer(L, xs)
+    lrms = float(np.sqrt(np.mean(ref["logits"].astype(np.float64) ** 2)))
+    lerr = float(np.abs(l_gpu - ref["logits"]).max()) / lrms
+    r.logits.copy_(torch.from_numpy(ref["logits"]))
+    y2 = q4.decode_tokens(layer, xd, ws, routing=r, logits_in=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.topk_idx.cpu().numpy(), ref["idx"])
+    assert np.abs(r.topk_w.cpu().numpy() - ref["w"]).max() <= W_TOL
+    err, rms = y_error(host_bits(y2), ref["y_exact"])
+    log(f"decode_tokens {name} T={T}: logits err/rms={lerr:.2e}, y err/rms={err:.3e}, rms {rms:.3f}")
+    assert lerr <= LOGIT_TOL
+    assert err <= Y_TOL
+
+
+def test_decode_tokens_workload(dev):
+    # the decode workload's layer 3 on T = 2, 3, 5 and 8 of its step inputs
+    w = WORKLOADS["decode"]
+    L, _ = make_layer(w, 3)
+    xs = decode_inputs(w, 8)
+    for T in (2, 3, 5, 8):
+        _decode_tokens_case(L, xs[:T], dev, "decode workload")
+
+
+def test_decode_tokens_small_shapes(dev):
+    rng = np.random.default_rng(11)
+    for T, d, inter, E, k, bias in ((3, 320, 128, 37, 5, True), (8, 256, 128, 8, 8, False),
+                                    (1, 576, 192, 40, 3, True), (6, 512, 64, 16, 1, False)):
+        L = random_layer(rng, d, inter, E, k, router_bias=bias)
+        _decode_tokens_case(L, random_x(rng, T, d), dev, f"d={d} I={inter} E={E} k={k}")
+
+
 # ------------------------------------------------------------------ edge cases
 
 EDGE = [
