@@ -336,7 +336,7 @@ def bench_decode(args, q4, torch, ev, stream):
     # the few-token decode shape: moe_decode_tokens on T tokens per call
     out["tokens"] = []
     for T in (2, 4, 8):
-        if args.decode_steps < 4:
+        if args.decode_steps < 4 or args.no_decode_tokens:
             break
         xt = torch.from_numpy(decode_inputs(w, 8 * 32).view(np.int16)).to(dev).view(torch.bfloat16)
         n_st = max(2, n_steps // 4)
@@ -485,6 +485,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-decode-tokens", action="store_true",
+                    help="skip the few-token decode figures (T = 2, 4, 8)")
     ap.add_argument("--sweep", default=None, metavar="T1,T2,...",
                     help="only the prefill sweep over these chunk sizes (balanced and skewed)")
     ap.add_argument("--copy-calibration", action="store_true",
