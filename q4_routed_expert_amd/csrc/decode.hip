@@ -108,6 +108,9 @@ __device__ __forceinline__ void gate_up_rows(const DecodeArgs& a, const uint16_t
             usr[r] = a.up.scale[so];
             ubr[r] = a.up.bias[so];
         }
+        // every load of the R rows is in flight before any of them is used
+        // (otherwise the compiler waits for each scale load on its own)
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 xv[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) xv[p] = ((const u32x4*)(s_x + kk))[p];
@@ -343,8 +346,8 @@ __global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeA
 // One wave per NO outputs n (n = first + 8 o); lane covers 8 consecutive
 // intermediate k (one code word) of each 512-wide pass, for every slot.  All
 // slots' loads are issued before the arithmetic; the combine then adds
-// w_s * P_s in slot order and the shared expert last.  NO grows with T so
-// that the grid stays about two work groups per CU.
+// w_s * P_s in slot order and the shared expert last.  NO = 2 for larger T
+// (fewer, fuller work groups; at 4 the registers spill).
 template <int NO>
 __global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(const DecodeArgs a) {
     // token t = blockIdx.y: h of its k + 1 experts, staged once per work group
@@ -441,12 +444,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     // outputs per wave: about two work groups per CU in all
-    int NO = 1;
-    while (NO < 4 && ((a.d + kDownWaves - 1) / kDownWaves) * a.T > 512 * NO) NO *= 2;
+    const int NO = ((a.d + kDownWaves - 1) / kDownWaves) * a.T > 512 ? 2 : 1;
     const dim3 g3((a.d + kDownWaves * NO - 1) / (kDownWaves * NO), a.T);
     if (NO == 1) hipLaunchKernelGGL(decode_down_kernel<1>, g3, dim3(64 * kDownWaves), 0, s, a);
-    else if (NO == 2) hipLaunchKernelGGL(decode_down_kernel<2>, g3, dim3(64 * kDownWaves), 0, s, a);
-    else hipLaunchKernelGGL(decode_down_kernel<4>, g3, dim3(64 * kDownWaves), 0, s, a);
+    else hipLaunchKernelGGL(decode_down_kernel<2>, g3, dim3(64 * kDownWaves), 0, s, a);
     trace_point(s);
     return hipGetLastError();
 }
