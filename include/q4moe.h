@@ -199,8 +199,9 @@ int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_
    r->topk_idx [T][k] and r->topk_w [T][k] are written (MOE_LOGITS_IN: the
    logits are read).  ws must hold moe_workspace_bytes(L, 1) bytes; T outside
    1 .. MOE_MAX_DECODE_TOKENS is MOE_EUNSUPPORTED.  ([Lily-M5] "Decode:
-   minimize bytes per token"; its closing discussion of the small-batch and
-   verification shapes.) */
+   minimize bytes per token"; "What didn't work": verifying a few draft rows
+   at once, whose rows route to different experts and so read more expert
+   bytes.) */
 int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
                       const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
                       void* stream);
