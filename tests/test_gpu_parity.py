@@ -335,3 +335,42 @@ def test_small_decode_shapes(dev):
         err, _ = y_error(host_bits(y), ref["y_exact"])
         log(f"decode d={d} I={inter} E={E} k={k}: y err/rms={err:.3e}")
         assert err <= Y_TOL
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_replays_match_eager(dev):
+    # One prefill layer call (route + prefill) and one few-token decode call
+    # captured in a HIP graph; every replay, with eager calls on other inputs
+    # in between, must reproduce the eager outputs bit for bit.
+    rng = np.random.default_rng(21)
+    T, d, inter, E, k = 300, 256, 128, 32, 4
+    L = random_layer(rng, d, inter, E, k, router_bias=True)
+    layer = q4.DeviceLayer.from_host(L, dev)
+    xa, xb = xdev(random_x(rng, T, d), dev), xdev(random_x(rng, T, d), dev)
+    r = q4.DeviceRouting(T, E, k, dev)
+    ws = q4.workspace(layer, T, dev)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((5, d), dtype=torch.bfloat16, device=dev)
+    gx = xa.clone()
+
+    def calls(x_in):
+        q4.route(layer, x_in, routing=r)
+        q4.prefill(layer, x_in, r, ws, y)
+        q4.decode_tokens(layer, x_in[:5], ws, yd)
+
+    calls(gx)
+    torch.cuda.synchronize()
+    y_ref, yd_ref = host_bits(y), host_bits(yd)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(gx)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        calls(xb)  # eager work on other inputs between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y), y_ref), f"prefill replay {rep}"
+        assert np.array_equal(host_bits(yd), yd_ref), f"decode replay {rep}"
+    log("graph replays: prefill and few-token decode equal to eager on 3 replays")
