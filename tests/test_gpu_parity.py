@@ -243,7 +243,9 @@ def test_decode_tokens_workload(dev):
 def test_decode_tokens_small_shapes(dev):
     rng = np.random.default_rng(11)
     for T, d, inter, E, k, bias in ((3, 320, 128, 37, 5, True), (8, 256, 128, 8, 8, False),
-                                    (1, 576, 192, 40, 3, True), (6, 512, 64, 16, 1, False)):
+                                    (1, 576, 192, 40, 3, True), (6, 512, 64, 16, 1, False),
+                                    (8, 8192, 128, 8, 2, False),   # the largest d, 8 tokens
+                                    (2, 1024, 2048, 16, 8, True)):  # the largest inter
         L = random_layer(rng, d, inter, E, k, router_bias=bias)
         _decode_tokens_case(L, random_x(rng, T, d), dev, f"d={d} I={inter} E={E} k={k}")
 
@@ -259,6 +261,9 @@ EDGE = [
     (100, 256, 128, 256, 8, False, 5),    # most experts empty
     (129, 256, 64, 16, 1, True, 6),       # k = 1, one row past a tile
     (90, 320, 128, 37, 5, True, 7),       # E not a multiple of 4 (router column loads), d = 5 x 64
+    (100, 512, 576, 8, 2, False, 8),      # inter > 512 and not a multiple of 512: chunked down GEMM
+    (70, 1024, 2048, 8, 2, True, 9),      # the largest inter (chunked down GEMM)
+    (40, 8192, 128, 8, 2, False, 10),     # the largest d
 ]
 
 
