@@ -457,8 +457,12 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     // the item cost prefix and the items' experts were computed by the
     // gate/up kernel (down_schedule) into the workspace
     for (int i = tid; i <= n_items; i += kThreads) {
-        s_pre[i] = a.dn_pre[i];
-        if (i < n_items) s_exp[i] = (short)a.dn_exp[i];
+        // both loads in flight before either is used (clamped, always valid)
+        const int pv = a.dn_pre[i];
+        const int ev = a.dn_exp[i < n_items ? i : 0];
+        asm volatile("" ::"v"(pv), "v"(ev));  // keeps the second load out of the branch below
+        s_pre[i] = pv;
+        if (i < n_items) s_exp[i] = (short)ev;
     }
     __syncthreads();
     const int u_first = run_start(g, G, n_items, n_cb, s_pre);

@@ -214,11 +214,23 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(
 
     // 1. totals and earlier-block counts
     if (tid < E) {
+        // sixteen blocks' counts in flight at a time (one load after another,
+        // each waited for, would cost one memory round trip per block)
         int tot = 0, before = 0;
-        for (int b = 0; b < n_blk; ++b) {
-            const int c = blk_counts[(size_t)b * E + tid];
-            before += b < g ? c : 0;
-            tot += c;
+        for (int b0 = 0; b0 < n_blk; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int b = b0 + u < n_blk ? b0 + u : 0;  // clamped, always valid
+                c[u] = blk_counts[(size_t)b * E + tid];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int b = b0 + u;
+                const int v = b < n_blk ? c[u] : 0;
+                before += b < g ? v : 0;
+                tot += v;
+            }
         }
         s_cnt[tid] = tot;
         s_before[tid] = before;
