@@ -276,8 +276,9 @@ def bench_decode(args, q4, torch, ev, stream):
     ws = q4.workspace(layers[0], 1, dev)
     y = torch.empty((1, w.d), dtype=torch.bfloat16, device=dev)
     lib = q4._abi.lib()
-    for li in range(n_layers):  # warm-up: one pass over all layers
-        q4.decode(layers[li], xs[0:1], ws, y)
+    for st in range(max(1, args.decode_warmup)):  # warm-up passes over all layers
+        for li in range(n_layers):
+            q4.decode(layers[li], xs[st % n_steps:st % n_steps + 1], ws, y)
     torch.cuda.synchronize()
     mid = n_steps // 2
     ev_d = [ev.make(4) for _ in range(n_layers)]
@@ -478,9 +479,13 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # about 60 ms of untimed layer calls: the first tens of calls run up to 15 %
+    # slower (clocks and caches settling), measured over 20 .. 400 warm-up calls
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--decode-layers", type=int, default=40)
+    ap.add_argument("--decode-warmup", type=int, default=1,
+                    help="untimed decode passes over the layers before the timed steps")
     ap.add_argument("--cpu-tokens", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
