@@ -56,6 +56,9 @@ def _load():
         lib.oracle_layer_tokens.argtypes = [C.POINTER(_Layer), vp, vp, i64, vp, vp, vp, vp]
         lib.oracle_threads.restype = C.c_int
         lib.oracle_bf16_round.argtypes = [vp, i64, vp]
+        lib.oracle_lm_logits.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+        lib.oracle_argmax.argtypes = [vp, i64]
+        lib.oracle_argmax.restype = i64
         _lib = lib
     return _lib
 
@@ -172,3 +175,38 @@ def layer(L: dict, x, logits=None, tokens=None):
     y_exact, y = layer_tokens(L, x, tokens, r["idx"], r["w"])
     r.update(logits=logits, y_exact=y_exact, y=y, tokens=np.asarray(tokens, np.int32))
     return r
+
+
+# ---- greedy decoding's token hand-off (page section "Decode: minimize bytes
+# per token": the GPU picks the argmax and writes the token ID into the next
+# step's input slot).  The head and the embedding table are V x d Q4 matrices.
+
+def lm_logits(x, q, scale, bias) -> np.ndarray:
+    """fp32 [V] logits of a [V, d] Q4 matrix (q: uint32 [V, d/8]) applied to x (bf16 [d])."""
+    x = _c(x, np.uint16).reshape(-1)
+    q, scale, bias = _c(q, np.uint32), _c(scale, np.uint16), _c(bias, np.uint16)
+    V, d = q.shape[0], q.shape[1] * 8
+    assert x.size == d
+    out = np.empty(V, np.float32)
+    _load().oracle_lm_logits(_p(q), _p(scale), _p(bias), V, d, _p(x), _p(out))
+    return out
+
+
+def argmax(logits) -> int:
+    """Index of the largest logit; equal logits: the lower index; NaN counts as -inf."""
+    lg = _c(logits, np.float32).reshape(-1)
+    return int(_load().oracle_argmax(_p(lg), lg.size))
+
+
+def embed_row(q, scale, bias, token: int) -> np.ndarray:
+    """The next step's input: bf16 bits [d] of row `token` of a Q4 embedding table."""
+    return dequant(q[token:token + 1], scale[token:token + 1], bias[token:token + 1])[0]
+
+
+def lm_step(head: dict, embed: dict | None, x):
+    """One greedy hand-off: (logits, token, next input or None).  head / embed:
+    dicts with q, scale, bias as above."""
+    lg = lm_logits(x, head["q"], head["scale"], head["bias"])
+    tok = argmax(lg)
+    nxt = None if embed is None else embed_row(embed["q"], embed["scale"], embed["bias"], tok)
+    return lg, tok, nxt

@@ -47,7 +47,8 @@
  *
  * Precision: every dot product accumulates in double, index ascending.  The
  * only roundings are the ones listed above plus the fp32 rounding of the
- * router logits (the router emits fp32 logits).
+ * router logits and of the output logits of the token hand-off (both are
+ * fp32 logits).
  */
 #include <math.h>
 #include <stdint.h>
@@ -302,4 +303,47 @@ int oracle_threads(void) { return 1; }
 /* Test hook: the bf16 rounding used throughout, on an array of doubles. */
 void oracle_bf16_round(const double* v, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(v[i]);
+}
+
+/* ---- O13-O15: greedy decoding's token hand-off --------------------------- */
+/* [Lily-M5, "Decode: minimize bytes per token"]: the token never goes back to
+   the CPU between decode steps; the GPU takes the argmax over the output
+   logits and puts the token ID straight into the input slot of the next step.
+   Readings (the pages give no further detail):
+     - the output projection ("LM head") and the input embedding table are V x d
+       matrices in the experts' group-64 Q4 format, used as bf16 weights;
+     - logit v = fp32( sum_j x[j] * w(v, j) ), summed in double, j ascending;
+     - the greedy token is the index of the largest logit, equal logits ordered
+       by the lower index, a NaN logit counting as minus infinity (so a vector of
+       V NaNs gives token 0);
+     - the next step's input is the token's embedding row, i.e. the dequantised
+       bf16 row (oracle_dequant of that one row). */
+
+/* O13: logits[v] for v = 0..V-1 of a [V][d] Q4 matrix applied to x (bf16 [d]). */
+void oracle_lm_logits(const uint32_t* q, const uint16_t* scale, const uint16_t* bias, int64_t V,
+                      int64_t d, const uint16_t* x, float* logits) {
+    if (d % GROUP) fail("d must be a multiple of 64");
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t v = 0; v < V; ++v) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < d; ++j)
+            acc += bf16_value(x[j]) * bf16_value(dequant_at(q, scale, bias, d, v, j));
+        logits[v] = (float)acc;
+    }
+}
+
+/* O14: the greedy token. */
+int64_t oracle_argmax(const float* logits, int64_t V) {
+    int64_t best = 0;
+    double best_v = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        const double lv = isnan(logits[v]) ? -INFINITY : (double)logits[v];
+        if (v == 0 || lv > best_v) {
+            best = v;
+            best_v = lv;
+        }
+    }
+    return best;
 }

@@ -376,3 +376,57 @@ def test_tiny_workload_layer_runs_and_is_deterministic():
     _check_sorted_order(a["idx"], a, w.n_experts)
     rms = np.sqrt(np.mean(a["y_exact"] ** 2))
     assert 0.05 < rms < 50
+
+
+# ---------------------------------------------------------------- token hand-off
+
+def test_lm_logits_match_float64_matmul():
+    rng = np.random.default_rng(7)
+    V, d = 37, 192  # V != d catches a transposed head
+    from workloads import random_lm
+    x, head, _ = random_lm(rng, V, d)
+    W = bits_to_f32(oracle.dequant(head["q"], head["scale"], head["bias"])).astype(np.float64)
+    ref = W @ bits_to_f32(x).astype(np.float64)
+    got = oracle.lm_logits(x, head["q"], head["scale"], head["bias"])
+    assert got.shape == (V,) and got.dtype == np.float32
+    assert np.all(np.abs(got - ref) <= 2 ** -23 * np.abs(ref) + 1e-30)
+
+
+def test_lm_logits_closed_form_per_row():
+    # row v: every code c_v = v % 16, scale 2^-7, bias -8 * 2^-7, so every weight is
+    # (c_v - 8) / 128 exactly; with x = 1 the logit is d * (c_v - 8) / 128.
+    V, d = 40, 256
+    codes = np.arange(V) % 16
+    q = np.stack([np.full(d // 8, _word([c] * 8), np.uint32) for c in codes])
+    s = np.full((V, d // 64), 0x3C00, np.uint16)
+    b = np.full((V, d // 64), 0xBD80, np.uint16)
+    x = np.full(d, 0x3F80, np.uint16)  # bf16 1.0
+    got = oracle.lm_logits(x, q, s, b)
+    assert np.array_equal(got, (d * (codes - 8) / 128).astype(np.float32))
+    # greedy token: code 15 first appears at v = 15; the next input is its row
+    lg, tok, nxt = oracle.lm_step({"q": q, "scale": s, "bias": b}, {"q": q, "scale": s, "bias": b}, x)
+    assert tok == 15
+    assert np.all(bits_to_f32(nxt) == np.float32(7 / 128))
+
+
+@pytest.mark.parametrize("vals,want", [
+    ([1, 3, 3, 2], 1),                          # equal maxima: the lower index
+    ([float("nan"), -1, -2], 1),                # NaN counts as -inf
+    ([float("nan")] * 5, 0),                    # all NaN: token 0
+    ([-math.inf] * 3, 0),
+    ([-math.inf, float("nan"), -5], 2),
+    ([-0.0, 0.0], 0),                           # signed zeros are equal
+    ([0.0, -0.0, 1e-45], 2),                    # the smallest subnormal beats zero
+    ([2, float("nan"), 2], 0),
+    ([5], 0),
+    ([3.4e38, math.inf, 1], 1),
+])
+def test_argmax_hand_cases(vals, want):
+    assert oracle.argmax(np.array(vals, np.float32)) == want
+
+
+def test_argmax_matches_numpy_first_occurrence():
+    rng = np.random.default_rng(3)
+    for V in (1, 2, 1000, 100003):
+        l = np.round(rng.standard_normal(V) * 4).astype(np.float32)  # many ties
+        assert oracle.argmax(l) == int(np.argmax(l))

@@ -152,3 +152,41 @@ def random_layer(rng: np.random.Generator, d: int, inter: int, E: int, k: int,
 
 def random_x(rng: np.random.Generator, T: int, d: int) -> np.ndarray:
     return bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+
+
+# ---- the greedy token hand-off (section "Decode: minimize bytes per token":
+# the GPU takes the argmax of the output logits and writes the token ID into
+# the next step's input slot).  The pages give neither the vocabulary size nor
+# the format of the output head and the embedding table; both are taken as
+# V x d matrices in the experts' Q4 format, with the experts' value
+# distributions.  Draw order from PCG64(seed): x, head, embedding table.
+
+@dataclass(frozen=True)
+class LmWorkload:
+    name: str
+    V: int
+    d: int
+    seed: int
+    note: str = ""
+
+
+LM_WORKLOADS = {
+    "lm_tiny": LmWorkload("lm_tiny", V=3000, d=512, seed=20,
+                          note="small head, checkable on the CPU in well under a second"),
+    "lm_head": LmWorkload("lm_head", V=248320, d=2048, seed=21,
+                          note="the layer's hidden size and a vocabulary of 248,320 rows"),
+}
+
+
+def random_lm(rng: np.random.Generator, V: int, d: int):
+    """(x bf16 [d], head, embed) with head / embed dicts of q [V, d/8], scale, bias."""
+    x = bf16_bits(rng.standard_normal(d, dtype=np.float32))
+    out = []
+    for _ in range(2):
+        q, s, b = q4_matrix(rng, 1, V, d)
+        out.append({"q": q[0], "scale": s[0], "bias": b[0]})
+    return x, out[0], out[1]
+
+
+def make_lm(w: LmWorkload):
+    return random_lm(np.random.Generator(np.random.PCG64(w.seed)), w.V, w.d)
