@@ -104,26 +104,29 @@ def prefill_work(T, d, I, E, k, counts):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gate_up_T2048_decode.md")
 KERNEL_SOURCES = ("q4_routed_expert_amd/csrc/prefill.hip", "q4_routed_expert_amd/csrc/decode.hip",
                   "q4_routed_expert_amd/csrc/q4moe_dev.h", "q4_routed_expert_amd/csrc/internal.h")
+LM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_lm_head_V248320.md")
+LM_SOURCES = ("q4_routed_expert_amd/csrc/lmhead.hip", "q4_routed_expert_amd/csrc/lmhead.h",
+              "q4_routed_expert_amd/csrc/q4moe_dev.h", "q4_routed_expert_amd/csrc/internal.h")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(key):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
+def measured_traffic(key, path=None, sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
     when the summary is missing or the kernel sources have changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             for line in f:
                 if line.startswith("traffic-json: "):
                     rec = json.loads(line[len("traffic-json: "):])
-                    if rec.get("source_hash") == kernel_source_hash() and key in rec:
+                    if rec.get("source_hash") == kernel_source_hash(sources) and key in rec:
                         return rec[key]
     except OSError:
         pass
@@ -395,6 +398,67 @@ def bench_decode(args, q4, torch, ev, stream):
     return out
 
 
+def bench_handoff(args, q4, torch, ev, stream):
+    """Greedy token hand-off (moe_lm_argmax) at V = 248,320, d = 2048: a chain of
+    steps, each reading the previous step's embedding row as its input and
+    writing its token into one of two slots, with no host synchronisation."""
+    from workloads import LM_WORKLOADS, make_lm
+    w = LM_WORKLOADS["lm_head"]
+    log(f"hand-off: generating the output head and embedding table (V={w.V}, d={w.d})")
+    x, head, embed = make_lm(w)
+    dev = torch.device("cuda:0")
+    lm = q4.DeviceLmHead.from_host(head, embed, dev)
+    del head, embed
+    ws = q4.lm_workspace(lm, dev)
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16),
+          torch.empty(w.d, dtype=torch.bfloat16, device=dev)]
+    logits = torch.empty(w.V, dtype=torch.float32, device=dev)
+    slots = torch.zeros(2, dtype=torch.int32, device=dev)
+    lib = q4._abi.lib()
+
+    def step(i):
+        q4.lm_argmax(lm, xs[i % 2], ws, logits=logits, token=slots[i % 2:i % 2 + 1],
+                     x_next=xs[(i + 1) % 2])
+
+    for i in range(20):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(20, args.steps * 4)
+    t = ev.make(2)
+    ev.record(t[0], stream)
+    for i in range(n):
+        step(i)
+    ev.record(t[1], stream)
+    torch.cuda.synchronize()
+    us = ev.ms(t[0], t[1]) * 1e3 / n
+    n_tr = 20
+    evs = [ev.make(3) for _ in range(n_tr)]
+    for i in range(n_tr):
+        lib.moe_trace_events(C.cast(evs[i], C.c_void_p), 3)
+        step(i)
+        lib.moe_trace_events(None, 0)
+    torch.cuda.synchronize()
+    per = {nm: sum(ev.ms(evs[i][j], evs[i][j + 1]) for i in range(n_tr)) * 1e3 / n_tr
+           for j, nm in enumerate(("lm_head", "pick_embed"))}
+    n_part = -(-w.V // 32)
+    # algorithmic bytes of the head kernel: every code, scale and bias once, x,
+    # the logits and the partial results written
+    head_bytes = q4_bytes(w.V, w.d) + 2 * w.d + 4 * w.V + 8 * n_part
+    gbps = head_bytes / (per["lm_head"] * 1e-6) / 1e9
+    log(f"hand-off: {us:.2f} us/step, per kernel (us): " +
+        ", ".join(f"{k}={v:.2f}" for k, v in per.items()) + f"; head {gbps:.0f} GB/s")
+    out = {"V": w.V, "d": w.d, "us_per_step": round(us, 3), "steps": n,
+           "kernel_us": {k: round(v, 3) for k, v in per.items()},
+           "head_bytes": head_bytes,
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                        "traffic": measured_traffic("lm_head_bytes", LM_TRAFFIC_FILE, LM_SOURCES),
+                        "kernel": "lm_head_kernel (Q4 output-head GEMV + partial argmax)"}}
+    del lm, ws, xs, logits
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_sweep(args, q4, torch, ev, stream):
     """Prefill layer time over chunk sizes T (balanced and skewed router), the
     small-T verify shapes (T = 1..8 through the same prefill path) included.
@@ -490,6 +554,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-handoff", action="store_true",
+                    help="skip the greedy token hand-off (output head + argmax) measurement")
     ap.add_argument("--no-decode-tokens", action="store_true",
                     help="skip the few-token decode figures (T = 2, 4, 8)")
     ap.add_argument("--sweep", default=None, metavar="T1,T2,...",
@@ -523,6 +589,7 @@ def main():
         return
     pre = bench_prefill(args, q4, torch, ev, stream)
     dec = None if args.no_decode else bench_decode(args, q4, torch, ev, stream)
+    hand = None if args.no_handoff else bench_handoff(args, q4, torch, ev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
     ev.close()
     w = pre["workload"]
@@ -559,6 +626,9 @@ def main():
                                        for k, v in dec["graph"].items()}
         line["decode"]["tokens"] = dec["tokens"]
         line["roofline_decode"] = dec["roofline"]
+    if hand is not None:
+        line["handoff"] = {k: v for k, v in hand.items() if k != "roofline"}
+        line["roofline_handoff"] = hand["roofline"]
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

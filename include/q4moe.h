@@ -206,19 +206,50 @@ int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t
                       const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
                       void* stream);
 
+/* Greedy decoding's token hand-off ([Lily-M5] "Decode: minimize bytes per
+   token": the token ID never goes back to the CPU between decode steps; the GPU
+   takes the argmax of the output logits and writes the token straight into the
+   next step's input slot).  The output head and the input embedding table are
+   V x d matrices in the moe_q4mat format above (matrix 0 of each), used as
+   bf16 weights like the experts' (the pages give no format of their own). */
+#define MOE_MAX_VOCAB 1048576
+typedef struct {
+    int32_t V;          /* vocabulary rows, 1 <= V <= MOE_MAX_VOCAB */
+    int32_t d;          /* hidden size, a multiple of 64, <= MOE_MAX_D */
+    moe_q4mat head;     /* [V][d]: logit v = sum_k w(v, k) * x[k] */
+    moe_q4mat embed;    /* [V][d]: row v is token v's input; may be all NULL when
+                           moe_lm_argmax gets x_next = NULL */
+} moe_lm_head;
+/* Workspace bytes of moe_lm_argmax for this head (per-work-group partial
+   results); 0 on invalid arguments.  Needs no initialisation, not preserved. */
+size_t moe_lm_workspace_bytes(const moe_lm_head* lm);
+/* One hand-off, two kernels, no host synchronisation:
+     logits[v] = fp32 sum over k of bf16(head weight) * x[k]   (unless MOE_LOGITS_IN)
+     *token    = the v with the largest logit; equal logits: the lower v; a NaN
+                 logit counts as minus infinity (V NaNs give token 0)
+     x_next    = bf16 row *token of embed (the next decode step's input), if
+                 x_next is not NULL
+   x: bf16 [d] (unused, may be NULL, with MOE_LOGITS_IN); logits: fp32 [V],
+   written, or read with MOE_LOGITS_IN; token: one int32, only 4-byte aligned
+   (so the caller can alternate between two slots of one array, one per step);
+   x_next: bf16 [d], may be the same buffer as x.  ws must hold
+   moe_lm_workspace_bytes(lm) bytes.  Unknown flags are MOE_EINVAL. */
+int moe_lm_argmax(const moe_lm_head* lm, const uint16_t* x, uint32_t flags, float* logits,
+                  int32_t* token, uint16_t* x_next, void* ws, size_t ws_bytes, void* stream);
 /* The on-chip dequantisation the GEMMs use, exposed for testing: w_out (bf16
    [n_rows][K]) = bf16(q * scale + bias) for matrix 0 of m.  K % 64 == 0. */
 int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, void* stream);
 
-/* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill and
-   moe_decode call made on this host thread records events[0] on its stream
+/* Timing hook.  While `events` is non-NULL, every moe_route, moe_prefill,
+   moe_decode, moe_decode_tokens and moe_lm_argmax call made on this host thread records events[0] on its stream
    before its first kernel and events[i] right after its i-th kernel, for
    i < n (moe_route: router logits (with MOE_LOGITS_IN: the clearing of
    the histogram), top-k + histogram, scan + scatter + maps;
    moe_prefill: gate/up, down
    (routed and shared), combine; moe_decode and moe_decode_tokens: router
    partial sums + shared gate/up, logits + top-k + routed gate/up, down +
-   combine).  The
+   combine; moe_lm_argmax: output head (with MOE_LOGITS_IN: the scan of the
+   given logits), pick + embedding row).  The
    elapsed time between consecutive events is one kernel's duration.  events
    are hipEvent_t handles created and owned by the caller; pass NULL to stop. */
 void moe_trace_events(void* const* events, int32_t n);

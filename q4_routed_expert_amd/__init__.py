@@ -8,6 +8,8 @@ stream.  There is no fallback: if the library is missing, loading raises.
     r = route(layer, x)                        # x: bf16 [T, d] on the GPU
     y = prefill(layer, x, r)                   # bf16 [T, d]
     y1 = decode(layer, x1, ws)                 # one token
+    lm = DeviceLmHead.from_host(head, embed)     # V x d output head, embedding
+    logits, tok, _ = lm_argmax(lm, h, lm_workspace(lm), x_next=x_in)  # greedy token
 """
 from __future__ import annotations
 
@@ -176,6 +178,51 @@ def dequant(q: torch.Tensor, scale: torch.Tensor, bias: torch.Tensor, stream=Non
     m = _abi.Q4Mat(_ptr(q), _ptr(scale), _ptr(bias))
     _check(_abi.lib().moe_dequant(C.addressof(m), N, K, _ptr(out), _stream(stream)), "moe_dequant")
     return out
+
+
+class DeviceLmHead:
+    """An output head and embedding table (V x d Q4 each) in device memory, plus
+    the moe_lm_head struct pointing at them."""
+
+    def __init__(self, V: int, d: int, head: dict, embed: dict | None):
+        self.V, self.d = V, d
+        self.head, self.embed = head, embed  # keep the tensors alive
+
+        def mat(m):
+            return _abi.Q4Mat() if m is None else _abi.Q4Mat(_ptr(m["q"]), _ptr(m["scale"]),
+                                                              _ptr(m["bias"]))
+        self.struct = _abi.LmHead(V, d, mat(head), mat(embed))
+
+    @classmethod
+    def from_host(cls, head: dict, embed: dict | None = None, device="cuda"):
+        """head / embed: dicts of numpy q uint32 [V, d/8], scale, bias uint16 [V, d/64]."""
+        V, d = head["q"].shape[0], head["q"].shape[1] * 8
+        dev = lambda m: None if m is None else {k: _dev(m[k], device) for k in ("q", "scale", "bias")}
+        return cls(V, d, dev(head), dev(embed))
+
+
+def lm_workspace(lm: DeviceLmHead, device="cuda") -> torch.Tensor:
+    n = _abi.lib().moe_lm_workspace_bytes(C.addressof(lm.struct))
+    if n == 0:
+        raise MoEError(_abi.MOE_EINVAL, "moe_lm_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lm_argmax(lm: DeviceLmHead, x: torch.Tensor | None, ws: torch.Tensor,
+              logits: torch.Tensor | None = None, token: torch.Tensor | None = None,
+              x_next: torch.Tensor | None = None, logits_in: bool = False, stream=None):
+    """Greedy token hand-off: (logits fp32 [V], token int32 [1], x_next or None).
+    With logits_in the given logits are read instead of computed from x."""
+    dev = ws.device
+    if logits is None:
+        logits = torch.empty(lm.V, dtype=torch.float32, device=dev)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=dev)
+    flags = MOE_LOGITS_IN if logits_in else 0
+    _check(_abi.lib().moe_lm_argmax(C.addressof(lm.struct), _ptr(x), flags, _ptr(logits),
+                                    _ptr(token), _ptr(x_next), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "moe_lm_argmax")
+    return logits, token, x_next
 
 
 def library_path() -> str:

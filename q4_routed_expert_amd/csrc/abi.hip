@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include "internal.h"
+#include "lmhead.h"
 
 namespace {
 
@@ -135,6 +136,19 @@ PrefillWs prefill_ws(const moe_layer* L, int32_t T, size_t base) {
 }
 
 q4moe::Q4 q4(const moe_q4mat& m) { return q4moe::Q4{m.q, m.scale, m.bias}; }
+
+int check_lm(const moe_lm_head* lm) {
+    if (!lm) return fail(MOE_EINVAL, "lm head is NULL");
+    if (lm->V <= 0 || lm->d <= 0) return fail(MOE_EINVAL, "V=%d and d=%d must be positive", lm->V, lm->d);
+    if (lm->d % MOE_GROUP || lm->d > MOE_MAX_D)
+        return fail(MOE_EUNSUPPORTED, "d=%d must be a multiple of %d and <= %d", lm->d, MOE_GROUP,
+                    MOE_MAX_D);
+    if (lm->V > MOE_MAX_VOCAB) return fail(MOE_EUNSUPPORTED, "V=%d > %d", lm->V, MOE_MAX_VOCAB);
+    return MOE_OK;
+}
+
+// Hand-off workspace: per-work-group best logits, then their rows.
+size_t lm_part_bytes(int32_t V) { return align256(sizeof(float) * q4moe::lm_partials(V, false)); }
 
 int hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -298,6 +312,42 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
     if (K % MOE_GROUP) return fail(MOE_EUNSUPPORTED, "K=%d not a multiple of %d", K, MOE_GROUP);
     return hip_status(q4moe::launch_dequant(q4(*m), n_rows, K, w_out, (hipStream_t)stream),
                       "dequant");
+}
+
+size_t moe_lm_workspace_bytes(const moe_lm_head* lm) {
+    if (check_lm(lm)) return 0;
+    return 2 * lm_part_bytes(lm->V);
+}
+
+int moe_lm_argmax(const moe_lm_head* lm, const uint16_t* x, uint32_t flags, float* logits,
+                  int32_t* token, uint16_t* x_next, void* ws, size_t ws_bytes, void* stream) {
+    int rc;
+    if ((rc = check_lm(lm))) return rc;
+    if (flags & ~MOE_LOGITS_IN) return fail(MOE_EINVAL, "unknown flags 0x%x", flags);
+    const bool logits_in = flags & MOE_LOGITS_IN;
+    if (!logits_in && ((rc = check_mat(lm->head, "head")) || (rc = check_ptr(x, "x")))) return rc;
+    if ((rc = check_ptr(logits, "logits")) || (rc = check_ptr(ws, "workspace"))) return rc;
+    if (!token || ((uintptr_t)token & 3u))
+        return fail(MOE_EINVAL, "token is NULL or not 4-byte aligned");
+    if (x_next && ((rc = check_ptr(x_next, "x_next")) || (rc = check_mat(lm->embed, "embed"))))
+        return rc;
+    const size_t need = moe_lm_workspace_bytes(lm);
+    if (ws_bytes < need)
+        return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    unsigned char* base = (unsigned char*)ws;
+    q4moe::LmArgs a;
+    a.x = x;
+    a.V = lm->V;
+    a.d = lm->d;
+    a.head = q4(lm->head);
+    a.embed = q4(lm->embed);
+    a.logits = logits;
+    a.token = token;
+    a.x_next = x_next;
+    a.part_v = (float*)base;
+    a.part_i = (int32_t*)(base + lm_part_bytes(lm->V));
+    trace_begin((hipStream_t)stream);
+    return hip_status(q4moe::launch_lm_argmax(a, logits_in, (hipStream_t)stream), "lm argmax");
 }
 
 const char* moe_strerror(int code) {

@@ -36,7 +36,8 @@ def test_header_limits_match_binding():
     text = open(HEADER).read()
     for name in ("MOE_GROUP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_TOKENS", "MOE_MAX_D",
                  "MOE_MAX_INTER", "MOE_BLOCK_ROWS", "MOE_TILE_ROWS", "MOE_ROUTE_BLOCK",
-                 "MOE_DECODE_ROUTER_ROWS", "MOE_MAX_DECODE_TOKENS", "MOE_LOGITS_IN"):
+                 "MOE_DECODE_ROUTER_ROWS", "MOE_MAX_DECODE_TOKENS", "MOE_LOGITS_IN",
+                 "MOE_MAX_VOCAB"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m, name
         if hasattr(_abi, name):
@@ -175,3 +176,54 @@ def test_strerror_names_every_code():
     lib = _abi.lib()
     names = {lib.moe_strerror(c) for c in (0, -1, -2, -3, -4)}
     assert len(names) == 5
+
+
+def _lm(V=248320, d=2048, embed=True):
+    m = _abi.Q4Mat(FAKE, FAKE, FAKE)
+    return _abi.LmHead(V, d, m, _abi.Q4Mat(FAKE, FAKE, FAKE) if embed else _abi.Q4Mat())
+
+
+def _lm_call(lm, x=FAKE, flags=0, logits=FAKE, token=FAKE, x_next=None, ws=FAKE, ws_bytes=1 << 30):
+    return _abi.lib().moe_lm_argmax(C.addressof(lm), x, flags, logits, token, x_next, ws, ws_bytes,
+                                    None)
+
+
+def test_lm_workspace_bytes():
+    lib = _abi.lib()
+    for V, parts in ((248320, 7760), (1, 1), (33, 2), (_abi.MOE_MAX_VOCAB, 32768)):
+        lm = _lm(V)
+        n = lib.moe_lm_workspace_bytes(C.addressof(lm))
+        assert 8 * parts <= n <= 8 * parts + 512, (V, n)
+    for bad in (_lm(0), _lm(d=100), _lm(_abi.MOE_MAX_VOCAB + 1), _lm(d=_abi.MOE_MAX_D + 64)):
+        assert lib.moe_lm_workspace_bytes(C.addressof(bad)) == 0
+    assert lib.moe_lm_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(V=0), _abi.MOE_EINVAL), (dict(d=-64), _abi.MOE_EINVAL),
+    (dict(d=100), _abi.MOE_EUNSUPPORTED), (dict(V=_abi.MOE_MAX_VOCAB + 1), _abi.MOE_EUNSUPPORTED),
+])
+def test_lm_argmax_rejects_unsupported_heads(kw, code):
+    assert _lm_call(_lm(**kw)) == code
+
+
+def test_lm_argmax_validates_before_launch():
+    lib = _abi.lib()
+    lm = _lm()
+    need = lib.moe_lm_workspace_bytes(C.addressof(lm))
+    assert _lm_call(lm, ws_bytes=need - 1) == _abi.MOE_EWORKSPACE
+    assert _lm_call(lm, flags=2) == _abi.MOE_EINVAL
+    assert _lm_call(lm, token=None) == _abi.MOE_EINVAL
+    assert _lm_call(lm, token=FAKE + 2) == _abi.MOE_EINVAL
+    assert b"token" in lib.moe_last_error()
+    # a token slot needs only 4-byte alignment: this call gets as far as the workspace check
+    assert _lm_call(lm, token=FAKE + 4, ws_bytes=need - 1) == _abi.MOE_EWORKSPACE
+    assert _lm_call(lm, x=None) == _abi.MOE_EINVAL
+    assert _lm_call(lm, logits=None) == _abi.MOE_EINVAL
+    assert _lm_call(lm, x_next=FAKE + 8) == _abi.MOE_EINVAL
+    assert _lm_call(_lm(embed=False), x_next=FAKE) == _abi.MOE_EINVAL
+    assert b"embed" in lib.moe_last_error()
+    # given logits need neither x nor the head
+    nohead = _abi.LmHead(1000, 512, _abi.Q4Mat(), _abi.Q4Mat())
+    assert _lm_call(nohead, x=None, flags=_abi.MOE_LOGITS_IN, ws_bytes=0) == _abi.MOE_EWORKSPACE
+    assert _lm_call(nohead, x=None, flags=0, ws_bytes=0) == _abi.MOE_EINVAL

@@ -178,15 +178,16 @@ LM_WORKLOADS = {
 }
 
 
-def random_lm(rng: np.random.Generator, V: int, d: int):
-    """(x bf16 [d], head, embed) with head / embed dicts of q [V, d/8], scale, bias."""
+def random_lm(rng: np.random.Generator, V: int, d: int, with_embed: bool = True):
+    """(x bf16 [d], head, embed) with head / embed dicts of q [V, d/8], scale, bias
+    (embed None without with_embed; x and head are the same either way)."""
     x = bf16_bits(rng.standard_normal(d, dtype=np.float32))
-    out = []
-    for _ in range(2):
+    out = [None, None]
+    for i in range(2 if with_embed else 1):
         q, s, b = q4_matrix(rng, 1, V, d)
-        out.append({"q": q[0], "scale": s[0], "bias": b[0]})
+        out[i] = {"q": q[0], "scale": s[0], "bias": b[0]}
     return x, out[0], out[1]
 
 
-def make_lm(w: LmWorkload):
-    return random_lm(np.random.Generator(np.random.PCG64(w.seed)), w.V, w.d)
+def make_lm(w: LmWorkload, with_embed: bool = True):
+    return random_lm(np.random.Generator(np.random.PCG64(w.seed)), w.V, w.d, with_embed)
