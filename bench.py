@@ -440,7 +440,7 @@ def bench_handoff(args, q4, torch, ev, stream):
     torch.cuda.synchronize()
     per = {nm: sum(ev.ms(evs[i][j], evs[i][j + 1]) for i in range(n_tr)) * 1e3 / n_tr
            for j, nm in enumerate(("lm_head", "pick_embed"))}
-    n_part = -(-w.V // 32)
+    n_part = -(-w.V // 16)
     # algorithmic bytes of the head kernel: every code, scale and bias once, x,
     # the logits and the partial results written
     head_bytes = q4_bytes(w.V, w.d) + 2 * w.d + 4 * w.V + 8 * n_part

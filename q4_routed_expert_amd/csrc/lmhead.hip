@@ -18,18 +18,23 @@
 // (logit, index) pairs, so every reduction order gives the same token.
 //
 // Kernel 1 is HBM-bound: V * (d/2 + d/16) bytes of weights stream through
-// once (286 MB at V = 248,320, d = 2048).  A wave computes eight rows at a
-// time; lane l covers columns 32l .. 32l + 31 of every row, so one 16-byte
-// load per row and lane brings a whole 1 KB row per wave, and all eight
-// rows' loads are in flight before the first is used.  The lane's slice of x
-// stays in registers for all eight rows.
+// once (286 MB at V = 248,320, d = 2048).  A wave computes four rows; lane l
+// covers columns 32l .. 32l + 31 of every row, so one 16-byte load per row
+// and lane brings a whole 1 KB row per wave, and all four rows' loads are in
+// flight before the first is used.  The lane's slice of x stays in registers.
+// Small work groups of four such waves, one per 16 rows, measured faster than
+// bigger ones, than more rows per wave, and than persistent waves that
+// double-buffer their loads (a work group waits for its slowest wave at its
+// final reduction; small, short work groups keep the CUs filled).  The dot
+// products stay on the vector ALUs (v_dot2_f32_bf16): a 16-row MFMA form
+// was slower, its loads spanning 16 rows at 64 bytes each.
 #include "lmhead.h"
 
 namespace q4moe {
 namespace {
 
 constexpr int kLmWaves = 4;                    // waves per work group of kernel 1
-constexpr int kLmRows = 8;                     // rows per wave
+constexpr int kLmRows = 4;                     // rows per wave
 constexpr int kLmWgRows = kLmWaves * kLmRows;  // rows per work group
 constexpr int kScanThreads = 256;
 constexpr int kScanPer = 8;                    // logits per thread of lm_scan_kernel

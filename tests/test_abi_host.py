@@ -190,7 +190,7 @@ def _lm_call(lm, x=FAKE, flags=0, logits=FAKE, token=FAKE, x_next=None, ws=FAKE,
 
 def test_lm_workspace_bytes():
     lib = _abi.lib()
-    for V, parts in ((248320, 7760), (1, 1), (33, 2), (_abi.MOE_MAX_VOCAB, 32768)):
+    for V, parts in ((248320, 15520), (1, 1), (257, 17), (_abi.MOE_MAX_VOCAB, 65536)):
         lm = _lm(V)
         n = lib.moe_lm_workspace_bytes(C.addressof(lm))
         assert 8 * parts <= n <= 8 * parts + 512, (V, n)
