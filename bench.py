@@ -440,6 +440,28 @@ def bench_handoff(args, q4, torch, ev, stream):
     torch.cuda.synchronize()
     per = {nm: sum(ev.ms(evs[i][j], evs[i][j + 1]) for i in range(n_tr)) * 1e3 / n_tr
            for j, nm in enumerate(("lm_head", "pick_embed"))}
+    # the same chain captured in a HIP graph (8 steps) and replayed
+    graph = None
+    if not getattr(args, "no_graph", False):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(8):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(5, n // 8)
+        tg = ev.make(2)
+        gs = int(torch.cuda.current_stream().cuda_stream)
+        ev.record(tg[0], gs)
+        for _ in range(reps):
+            g.replay()
+        ev.record(tg[1], gs)
+        torch.cuda.synchronize()
+        graph = {"us_per_step": round(ev.ms(tg[0], tg[1]) * 1e3 / (8 * reps), 3),
+                 "steps": 8 * reps}
+        log(f"hand-off graph: {graph['us_per_step']:.2f} us/step")
+        del g
     n_part = -(-w.V // 16)
     # algorithmic bytes of the head kernel: every code, scale and bias once, x,
     # the logits and the partial results written
@@ -449,7 +471,7 @@ def bench_handoff(args, q4, torch, ev, stream):
         ", ".join(f"{k}={v:.2f}" for k, v in per.items()) + f"; head {gbps:.0f} GB/s")
     out = {"V": w.V, "d": w.d, "us_per_step": round(us, 3), "steps": n,
            "kernel_us": {k: round(v, 3) for k, v in per.items()},
-           "head_bytes": head_bytes,
+           "head_bytes": head_bytes, "graph": graph,
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                         "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                         "traffic": measured_traffic("lm_head_bytes", LM_TRAFFIC_FILE, LM_SOURCES),

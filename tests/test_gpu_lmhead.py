@@ -183,3 +183,48 @@ def _given_cases():
 def test_given_logits_token_is_exact(dev, name, lg):
     log(f"given logits {name} V={lg.size}")
     assert _given(dev, lg) == oracle.argmax(lg)
+
+
+def test_graph_replays_of_the_chain_match_eager(dev):
+    # two hand-off steps captured once; each replay continues the chain from where
+    # the previous one left it, and must match the same steps run eagerly
+    V, d = 3000, 512
+    x0, head, embed = random_lm(np.random.default_rng(13), V, d)
+    lm = q4.DeviceLmHead.from_host(head, embed, dev)
+    ws = q4.lm_workspace(lm, dev)
+    logits = torch.empty(V, dtype=torch.float32, device=dev)
+
+    def chain(xs, slots, n, stream=None):
+        for step in range(n):
+            q4.lm_argmax(lm, xs[step % 2], ws, logits=logits,
+                         token=slots[step % 2:step % 2 + 1], x_next=xs[(step + 1) % 2],
+                         stream=stream)
+
+    xs_e = [xdev(x0, dev), torch.empty(d, dtype=torch.bfloat16, device=dev)]
+    slots_e = torch.full((2,), -1, dtype=torch.int32, device=dev)
+    want = []
+    for rep in range(4):
+        chain(xs_e, slots_e, 2)
+        torch.cuda.synchronize()
+        want.append((slots_e.cpu().numpy().copy(), host_bits(xs_e[0]).copy()))
+    xs = [xdev(x0, dev), torch.empty(d, dtype=torch.bfloat16, device=dev)]
+    slots = torch.full((2,), -1, dtype=torch.int32, device=dev)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain([xs[0].clone(), xs[1].clone()], slots.clone(), 2)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        chain(xs, slots, 2)
+    xs[0].copy_(xdev(x0, dev))
+    slots.fill_(-1)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = torch.zeros(16, device=dev).sum()  # eager work between replays
+        log(f"replay {rep}: slots {slots.cpu().numpy().tolist()} want {want[rep][0].tolist()}")
+        assert np.array_equal(slots.cpu().numpy(), want[rep][0])
+        assert np.array_equal(host_bits(xs[0]), want[rep][1])
