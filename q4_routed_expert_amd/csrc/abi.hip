@@ -147,8 +147,8 @@ int check_lm(const moe_lm_head* lm) {
     return MOE_OK;
 }
 
-// Hand-off workspace: per-work-group best logits, then their rows.
-size_t lm_part_bytes(int32_t V) { return align256(sizeof(float) * q4moe::lm_partials(V, false)); }
+// Hand-off workspace: per-work-group best (logit, row) pairs.
+size_t lm_part_bytes(int32_t V) { return align256(8 * (size_t)q4moe::lm_partials(V, false)); }
 
 int hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -316,7 +316,7 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
 
 size_t moe_lm_workspace_bytes(const moe_lm_head* lm) {
     if (check_lm(lm)) return 0;
-    return 2 * lm_part_bytes(lm->V);
+    return lm_part_bytes(lm->V);
 }
 
 int moe_lm_argmax(const moe_lm_head* lm, const uint16_t* x, uint32_t flags, float* logits,
@@ -344,8 +344,7 @@ int moe_lm_argmax(const moe_lm_head* lm, const uint16_t* x, uint32_t flags, floa
     a.logits = logits;
     a.token = token;
     a.x_next = x_next;
-    a.part_v = (float*)base;
-    a.part_i = (int32_t*)(base + lm_part_bytes(lm->V));
+    a.part = (int2*)base;
     trace_begin((hipStream_t)stream);
     return hip_status(q4moe::launch_lm_argmax(a, logits_in, (hipStream_t)stream), "lm argmax");
 }

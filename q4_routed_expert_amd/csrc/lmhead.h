@@ -12,8 +12,7 @@ struct LmArgs {
     float* logits;       // [V]: written, or read when the logits are given
     int32_t* token;      // [1] the greedy token
     uint16_t* x_next;    // bf16 [d] the token's embedding row, or NULL
-    float* part_v;       // [lm_partials(V, .)] per-work-group best logit
-    int32_t* part_i;     // [lm_partials(V, .)] and its row
+    int2* part;          // [lm_partials(V, .)] per-work-group best (logit bits, row)
 };
 // Partial results the first kernel writes for V rows (given logits or not).
 int lm_partials(int V, bool logits_in);

@@ -39,7 +39,7 @@ constexpr int kLmWgRows = kLmWaves * kLmRows;  // rows per work group
 constexpr int kScanThreads = 256;
 constexpr int kScanPer = 8;                    // logits per thread of lm_scan_kernel
 constexpr int kPickThreads = 1024;
-constexpr int kPickBatch = 8;                  // partials a thread loads before comparing
+constexpr int kPickBatch = 16;                 // partials a thread loads before comparing
 
 __device__ __forceinline__ float pick_key(float v) { return v != v ? -INFINITY : v; }
 
@@ -64,8 +64,8 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
 // Best over the work group's waves (s_v / s_i hold one entry per wave); the
 // result goes to partial slot `slot`.  Called by every thread; contains a barrier.
 template <int NW>
-__device__ __forceinline__ void group_best(float v, int i, float* s_v, int* s_i, float* part_v,
-                                           int32_t* part_i, int slot) {
+__device__ __forceinline__ void group_best(float v, int i, float* s_v, int* s_i, int2* part,
+                                           int slot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) {
         s_v[wave] = v;
@@ -81,8 +81,7 @@ __device__ __forceinline__ void group_best(float v, int i, float* s_v, int* s_i,
                 bv = s_v[w];
                 bi = s_i[w];
             }
-        part_v[slot] = bv;
-        part_i[slot] = bi;
+        part[slot] = int2{__float_as_int(bv), bi};  // one 8-byte store
     }
 }
 
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(kLmWaves * 64) void lm_head_kernel(const LmArgs a) 
         }
     }
     if (lane < kLmRows && row0 + lane < V) a.logits[row0 + lane] = mine;
-    group_best<kLmWaves>(best, bi, s_v, s_i, a.part_v, a.part_i, blockIdx.x);
+    group_best<kLmWaves>(best, bi, s_v, s_i, a.part, blockIdx.x);
 }
 
 // Partials of given logits: work group b covers logits [b * 2048, +2048).
@@ -155,7 +154,7 @@ __global__ __launch_bounds__(kScanThreads) void lm_scan_kernel(const LmArgs a) {
             bi = i0 + j;
         }
     wave_best(best, bi);
-    group_best<kScanThreads / 64>(best, bi, s_v, s_i, a.part_v, a.part_i, blockIdx.x);
+    group_best<kScanThreads / 64>(best, bi, s_v, s_i, a.part, blockIdx.x);
 }
 
 // The greedy token from n_part partials, then the next step's input.
@@ -167,20 +166,19 @@ __global__ __launch_bounds__(kPickThreads) void lm_pick_kernel(const LmArgs a, i
     float best = -INFINITY;
     int bi = 0x7FFFFFFF;
     for (int p0 = 0; p0 < n_part; p0 += kPickThreads * kPickBatch) {
-        float pv[kPickBatch];
-        int pi[kPickBatch];
+        int2 pp[kPickBatch];
 #pragma unroll
         for (int u = 0; u < kPickBatch; ++u) {
             const int p = p0 + u * kPickThreads + tid;
             const int pc = p < n_part ? p : 0;  // clamped, always valid
-            pv[u] = a.part_v[pc];
-            pi[u] = a.part_i[pc];
+            pp[u] = a.part[pc];
         }
 #pragma unroll
         for (int u = 0; u < kPickBatch; ++u)
-            if (p0 + u * kPickThreads + tid < n_part && beats(pv[u], pi[u], best, bi)) {
-                best = pv[u];
-                bi = pi[u];
+            if (p0 + u * kPickThreads + tid < n_part &&
+                beats(__int_as_float(pp[u].x), pp[u].y, best, bi)) {
+                best = __int_as_float(pp[u].x);
+                bi = pp[u].y;
             }
     }
     wave_best(best, bi);

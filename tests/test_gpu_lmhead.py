@@ -78,7 +78,8 @@ def run_case(dev, x, head, embed, alias=False):
 
 
 @pytest.mark.parametrize("V,d,seed", [(1, 64, 0), (33, 192, 1), (2049, 2048, 2), (1000, 4160, 3),
-                                      (65, 8192, 4), (31, 512, 5), (4097, 1024, 6)])
+                                      (65, 8192, 4), (31, 512, 5), (4097, 1024, 6),
+                                      (q4._abi.MOE_MAX_VOCAB, 64, 7)])
 def test_small_heads(dev, V, d, seed):
     log(f"V={V} d={d} seed={seed}")
     x, head, embed = random_lm(np.random.default_rng(seed), V, d)
