@@ -17,8 +17,10 @@
 // NaN logit counting as minus infinity.  That is a strict total order on
 // (logit, index) pairs, so every reduction order gives the same token.
 //
-// Kernel 1 is HBM-bound: V * (d/2 + d/16) bytes of weights stream through
-// once (286 MB at V = 248,320, d = 2048).  A wave computes four rows; lane l
+// Kernel 1 streams V * (d/2 + d/16) bytes of weights once (286 MB at
+// V = 248,320, d = 2048), and its vector-ALU work (the dequantisation and the
+// dot products, 23 instructions per 8 weights) takes about as long as that
+// stream at full rate, so it is bound by both.  A wave computes four rows; lane l
 // covers columns 32l .. 32l + 31 of every row, so one 16-byte load per row
 // and lane brings a whole 1 KB row per wave, and all four rows' loads are in
 // flight before the first is used.  The lane's slice of x stays in registers.
