@@ -51,6 +51,26 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _need(t, name: str, dtype, n: int):
+    """The C ABI sees only pointers, so the binding checks what the kernels will
+    touch: a contiguous tensor of `dtype` with at least n elements (and, through
+    _on_gpu, in device memory)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.numel() < n:
+        raise ValueError(f"{name}: {t.numel()} elements, the call touches {n}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+
+
 def _dev(a: np.ndarray, device) -> torch.Tensor:
     a = np.ascontiguousarray(a)
     view = {np.dtype(np.uint32): np.int32, np.dtype(np.uint16): np.int16}.get(a.dtype, a.dtype)
@@ -126,6 +146,11 @@ def route(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting | None = N
     T = x.shape[0]
     r = routing or DeviceRouting(T, layer.n_experts, layer.top_k, x.device)
     flags = MOE_LOGITS_IN if logits_in else 0
+    if not logits_in:
+        _need(x, "x", torch.bfloat16, T * layer.d)
+    _need(r.logits, "routing.logits", torch.float32, T * layer.n_experts)
+    _need(r.perm, "routing.perm", torch.int32, T * layer.top_k)
+    _on_gpu(x=None if logits_in else x, logits=r.logits)
     _check(_abi.lib().moe_route(C.addressof(layer.struct), _ptr(x), T, flags, C.addressof(r.struct),
                                 _stream(stream)), "moe_route")
     return r
@@ -139,6 +164,10 @@ def prefill(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting,
         ws = workspace(layer, T, x.device)
     if y is None:
         y = torch.empty((T, layer.d), dtype=torch.bfloat16, device=x.device)
+    _need(x, "x", torch.bfloat16, T * layer.d)
+    _need(y, "y", torch.bfloat16, T * layer.d)
+    _need(routing.perm, "routing.perm", torch.int32, T * layer.top_k)
+    _on_gpu(x=x, y=y, ws=ws, perm=routing.perm)
     _check(_abi.lib().moe_prefill(C.addressof(layer.struct), _ptr(x), T, C.addressof(routing.struct),
                                   _ptr(ws), ws.numel(), _ptr(y), _stream(stream)),
            "moe_prefill")
@@ -152,6 +181,12 @@ def decode(layer: DeviceLayer, x: torch.Tensor, ws: torch.Tensor, y: torch.Tenso
         y = torch.empty((1, layer.d), dtype=torch.bfloat16, device=x.device)
     flags = MOE_LOGITS_IN if logits_in else 0
     rs = C.addressof(routing.struct) if routing is not None else None
+    _need(x, "x", torch.bfloat16, layer.d)
+    _need(y, "y", torch.bfloat16, layer.d)
+    if routing is not None:
+        _need(routing.logits, "routing.logits", torch.float32, layer.n_experts)
+        _need(routing.topk_idx, "routing.topk_idx", torch.int32, layer.top_k)
+    _on_gpu(x=x, y=y, ws=ws)
     _check(_abi.lib().moe_decode(C.addressof(layer.struct), _ptr(x), flags, rs, _ptr(ws), ws.numel(),
                                  _ptr(y), _stream(stream)), "moe_decode")
     return y
@@ -166,6 +201,12 @@ def decode_tokens(layer: DeviceLayer, x: torch.Tensor, ws: torch.Tensor,
         y = torch.empty((T, layer.d), dtype=torch.bfloat16, device=x.device)
     flags = MOE_LOGITS_IN if logits_in else 0
     rs = C.addressof(routing.struct) if routing is not None else None
+    _need(x, "x", torch.bfloat16, T * layer.d)
+    _need(y, "y", torch.bfloat16, T * layer.d)
+    if routing is not None:
+        _need(routing.logits, "routing.logits", torch.float32, T * layer.n_experts)
+        _need(routing.topk_idx, "routing.topk_idx", torch.int32, T * layer.top_k)
+    _on_gpu(x=x, y=y, ws=ws)
     _check(_abi.lib().moe_decode_tokens(C.addressof(layer.struct), _ptr(x), T, flags, rs, _ptr(ws),
                                         ws.numel(), _ptr(y), _stream(stream)), "moe_decode_tokens")
     return y
@@ -219,6 +260,13 @@ def lm_argmax(lm: DeviceLmHead, x: torch.Tensor | None, ws: torch.Tensor,
     if token is None:
         token = torch.empty(1, dtype=torch.int32, device=dev)
     flags = MOE_LOGITS_IN if logits_in else 0
+    if not logits_in:
+        _need(x, "x", torch.bfloat16, lm.d)
+    _need(logits, "logits", torch.float32, lm.V)
+    _need(token, "token", torch.int32, 1)
+    if x_next is not None:
+        _need(x_next, "x_next", torch.bfloat16, lm.d)
+    _on_gpu(x=None if logits_in else x, logits=logits, token=token, x_next=x_next, ws=ws)
     _check(_abi.lib().moe_lm_argmax(C.addressof(lm.struct), _ptr(x), flags, _ptr(logits),
                                     _ptr(token), _ptr(x_next), _ptr(ws), ws.numel(),
                                     _stream(stream)), "moe_lm_argmax")
