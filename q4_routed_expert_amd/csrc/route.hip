@@ -68,8 +68,11 @@ __global__ __launch_bounds__(64 * kRtWaves) void router_logits_kernel(
     f32x16 acc0 = {}, acc1 = {};
     float wv[S][8];
     u32x4 av[S], bv[S];
+    // a lane reads 8 consecutive k from kk: kk + 8 <= kend always (kq is a
+    // multiple of 8, so the first 8 of the range are valid for any step that
+    // runs past it)
     auto load = [&](int st, int k) {
-        const int kk = (k + 8 * half < kend ? k : kbeg) + 8 * half;
+        const int kk = k + 8 * half + 8 <= kend ? k + 8 * half : kbeg;
         av[st] = *(const u32x4*)(x + (xoa + (uint32_t)kk));
         bv[st] = *(const u32x4*)(x + (xob + (uint32_t)kk));
         const uint32_t wk = wo + (uint32_t)kk * (uint32_t)E;
