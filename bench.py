@@ -3,7 +3,8 @@
 
 One step = one prefill layer call on the T=2048 chunk (moe_route + moe_prefill:
 router logits, top-8, histogram/scan/scatter/block maps, gate/up grouped GEMM
-with SiLU*up, routed down GEMM, shared down + fixed-order combine), inputs
+with SiLU*up, routed down GEMM, shared down GEMM with the fixed-order combine
+in its epilogue), inputs
 resident in HBM, two distinct weight sets alternated so the weights stream
 from HBM; only two events bracket the timed steps, and the per-kernel split
 comes from separate steps with an event after every kernel.  The same steps
@@ -94,10 +95,13 @@ def prefill_work(T, d, I, E, k, counts):
         "flops": f_gu + f_dn_routed + f_dn_shared,
         "bytes": gu_w + dn_w + 4 * d * E + x_b + y_b,
         "gate_up": {"flops": f_gu, "bytes": gu_w + x_b + h_b + hs_b},
-        "down": {"flops": f_dn_routed + f_dn_shared,
-                 "bytes": dn_w + h_b + hs_b + 2 * T * k * d + 4 * T * d},
-        "combine": {"flops": 2 * T * k * d + T * d,
-                    "bytes": 2 * T * k * d + 4 * T * d + 4 * T * k + y_b},
+        # routed rows -> fp16 staging rows (+ one exponent byte per 32 columns)
+        "down": {"flops": f_dn_routed,
+                 "bytes": touched * q4_bytes(d, I) + h_b + 2 * T * k * d + T * k * d // 32},
+        # shared expert's down GEMM, the staged rows read back, scores, y
+        "shared_down_combine": {"flops": f_dn_shared + 2 * T * k * d + T * d,
+                                "bytes": q4_bytes(d, I) + hs_b + 2 * T * k * d + T * k * d // 32
+                                + 4 * T * k + y_b},
     }
 
 
@@ -206,7 +210,7 @@ def bench_prefill(args, q4, torch, ev, stream):
         step(args.warmup + K + i, ev_r[i], ev_p[i])
     torch.cuda.synchronize()
     names_r = ["router_logits", "topk_histogram", "route_scatter"]
-    names_p = ["gate_up", "down", "combine"]
+    names_p = ["gate_up", "down", "shared_down_combine"]
     per = {n: 0.0 for n in names_r + names_p}
     for i in range(Kt):
         for j, n in enumerate(names_r):

@@ -4,22 +4,21 @@
  *
  * Sources.  [Lily-M5] is the page "Perplexity's Lily beats MLX-LM on MacBook
  * M5 because it only runs one model"; sections are named in quotes.
- *   - "Why Qwen3.6-35B-A3B is a weird workload": a router scores the experts,
- *     picks 8 of 256, and adds one shared expert that sees every token.
- *   - "Prefill: keep routing on the GPU, dequantize in flight": weights are
- *     groupwise affine 4-bit, each group of 64 sharing a bf16 scale and bias
- *     (w = q * scale + bias); the grouped GEMM dequantises one tile at a time
- *     on chip, accumulates in FP32, writes bf16 and never materialises the
- *     expanded weights; routing (histogram, prefix scan, scatter, block map)
- *     runs on the GPU inside the chunk's command stream with no CPU round
- *     trip; tiles of 32 rows.
- *   - "Decode: minimize bytes per token": batch-1 expert projections are
- *     bandwidth-bound matrix-vector products; expert input projections are
- *     fused with the gate activation, and the output projection with the
- *     routing scores and the shared expert.
- *   - "Setup": the runtime rejects any checkpoint that is not exactly the
- *     supported architecture and quantisation.  Every entry point here is
- *     likewise fail-closed: an unsupported shape is refused before anything
+ *   - "Why Qwen3.6-35B-A3B is a weird workload": 8 of 256 routed experts per
+ *     token plus 1 always-on shared expert.
+ *   - "Prefill: keep routing on the GPU, dequantize in flight": 4-bit codes
+ *     with an affine map per group of 64 (bf16 scale s and bias b,
+ *     w = q * s + b); the prefill GEMM expands one small tile at a time on
+ *     chip (FP32 sums, bf16 results, no expanded weight copy in memory); the
+ *     histogram, prefix scan, scatter and block map stay on the GPU in the
+ *     chunk's stream, with no host round trip; 32-row tiles.
+ *   - "Decode: minimize bytes per token": at batch 1 the expert products are
+ *     memory-bound matrix-vector products; the gate activation is folded into
+ *     the input projections, and the scores and the shared expert into the
+ *     output projection.
+ *   - "Setup": the engine accepts only the one architecture and quantisation
+ *     it was built for.  Every entry point here is likewise fail-closed: an
+ *     unsupported shape is refused before anything
  *     is enqueued.
  *
  * What the layer computes, per token t with input x_t (bf16, length d):
@@ -153,10 +152,11 @@ int32_t moe_block_map_capacity(int32_t T, int32_t top_k, int32_t n_experts, int3
 /* Bytes of device workspace moe_prefill (T tokens), moe_decode and
    moe_decode_tokens (up to MOE_MAX_DECODE_TOKENS tokens, whatever T) need for
    this layer shape: the gate/up activations h (bf16), the shared
-   expert's activations, the routed experts' fp16 outputs and the shared
-   expert's fp32 outputs before the combine, and the decode path's router
-   partial sums.  0 on invalid arguments.  The
-   contents need no initialisation and are not preserved between calls. */
+   expert's activations, the routed experts' outputs staged for the combine
+   (fp16 scaled by a power of two per 32 columns, so any finite fp32 value
+   keeps 11 significant bits), and the decode path's router partial sums.
+   0 on invalid arguments.  The contents need no initialisation and are not
+   preserved between calls. */
 size_t moe_workspace_bytes(const moe_layer* L, int32_t T);
 
 /* Routing of T tokens, entirely on the device, no host synchronisation:
@@ -169,9 +169,11 @@ int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
 
 /* The expert part of the layer for T tokens routed by moe_route: grouped
    gate/up GEMM with fused SiLU(gate)*up over the expert-sorted rows plus the
-   shared expert over all tokens, then the down projections of the routed rows
-   and of the shared expert, then the fixed-order combine (slots in order,
-   scores applied, shared expert last).  Dequantisation
+   shared expert over all tokens, then the down projection of the routed rows,
+   then the shared expert's down projection with the fixed-order combine fused
+   into it (slots in order, scores applied, shared expert last; [Lily-M5]
+   "Decode: minimize bytes per token": the output projection carries the
+   routing scores and the shared expert).  Three kernels.  Dequantisation
    happens on chip, tile by tile; accumulation is fp32; y: bf16 [T][d].
    ws must hold moe_workspace_bytes(L, T) bytes. */
 int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r,
@@ -207,9 +209,9 @@ int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t
                       void* stream);
 
 /* Greedy decoding's token hand-off ([Lily-M5] "Decode: minimize bytes per
-   token": the token ID never goes back to the CPU between decode steps; the GPU
-   takes the argmax of the output logits and writes the token straight into the
-   next step's input slot).  The output head and the input embedding table are
+   token": the chosen token stays on the device between decode steps -- the
+   largest output logit selects it and it feeds the following step's input
+   directly).  The output head and the input embedding table are
    V x d matrices in the moe_q4mat format above (matrix 0 of each), used as
    bf16 weights like the experts' (the pages give no format of their own). */
 #define MOE_MAX_VOCAB 1048576
@@ -245,8 +247,8 @@ int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, 
    before its first kernel and events[i] right after its i-th kernel, for
    i < n (moe_route: router logits (with MOE_LOGITS_IN: the clearing of
    the histogram), top-k + histogram, scan + scatter + maps;
-   moe_prefill: gate/up, down
-   (routed and shared), combine; moe_decode and moe_decode_tokens: router
+   moe_prefill: gate/up, routed down,
+   shared down + combine; moe_decode and moe_decode_tokens: router
    partial sums + shared gate/up, logits + top-k + routed gate/up, down +
    combine; moe_lm_argmax: output head (with MOE_LOGITS_IN: the scan of the
    given logits), pick + embedding row).  The

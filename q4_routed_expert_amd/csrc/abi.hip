@@ -117,7 +117,7 @@ DecodeWs decode_ws(const moe_layer* L) {
     return w;
 }
 struct PrefillWs {
-    size_t h, h_sh, part, sh_out, dn_pre, dn_exp, total;
+    size_t h, h_sh, part, pexp, dn_pre, dn_exp, total;
 };
 PrefillWs prefill_ws(const moe_layer* L, int32_t T, size_t base) {
     PrefillWs w;
@@ -126,9 +126,8 @@ PrefillWs prefill_ws(const moe_layer* L, int32_t T, size_t base) {
     w.h = o; o += align256(sizeof(uint16_t) * A * L->inter);
     w.h_sh = o; o += align256(sizeof(uint16_t) * (size_t)T * L->inter);
     w.part = o; o += align256(sizeof(uint16_t) * A * L->d);
-    w.sh_out = o; o += align256(sizeof(float) * (size_t)T * L->d);
-    const size_t n_items = (size_t)(T + MOE_TILE_ROWS - 1) / MOE_TILE_ROWS +
-                           (size_t)moe_block_map_capacity(T, L->top_k, L->n_experts, MOE_TILE_ROWS);
+    w.pexp = o; o += align256((size_t)T * (L->d / 32) * MOE_MAX_TOPK);
+    const size_t n_items = (size_t)moe_block_map_capacity(T, L->top_k, L->n_experts, MOE_TILE_ROWS);
     w.dn_pre = o; o += align256(sizeof(int32_t) * (n_items + 1));
     w.dn_exp = o; o += align256(sizeof(int32_t) * n_items);
     w.total = o;
@@ -238,7 +237,8 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
     a.h = (uint16_t*)(base + pw.h);
     a.h_sh = (uint16_t*)(base + pw.h_sh);
     a.part = (uint16_t*)(base + pw.part);
-    a.sh_out = (float*)(base + pw.sh_out);
+    a.pexp = (int8_t*)(base + pw.pexp);
+    a.sh_rows = 0;  // chosen by the launcher
     a.dn_pre = (int32_t*)(base + pw.dn_pre);
     a.dn_exp = (int32_t*)(base + pw.dn_exp);
     a.y = y;

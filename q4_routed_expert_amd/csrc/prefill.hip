@@ -1,10 +1,11 @@
 // prefill.hip -- the expert part of one MoE layer for a chunk of T tokens:
 //   (1) grouped gate/up GEMM over the expert-sorted rows, SiLU(gate)*up fused,
 //       plus the shared expert over all tokens            -> h, h_sh (bf16)
-//   (2) grouped down GEMM of the routed rows -> part (fp16, one row per
-//       assignment) and of the shared expert -> sh_out (fp32, one row per token)
-//   (3) the fixed-order combine:
-//       y_t = bf16( sum_s w[t,s] * part[t*k+s] (slot order) + sh_out[t] )
+//   (2) grouped down GEMM of the routed rows -> part (fp16 scaled by a power
+//       of two per 32 columns of a row, one row per assignment)
+//   (3) the shared expert's down GEMM with the fixed-order combine in its
+//       epilogue:
+//       y_t = bf16( sum_s w[t,s] * part[t*k+s] (slot order) + shared_t )
 // Sources: [Lily-M5] = "Perplexity's Lily beats MLX-LM on MacBook M5 because
 // it only runs one model".  Section "Prefill: keep routing on the GPU,
 // dequantize in flight": the grouped GEMM dequantises one small Q4 tile at a
@@ -14,7 +15,7 @@
 // expert.
 //
 // Kernel design (gfx950).  One work item = up to 128 rows of one expert (the
-// 128-row work map written by the routing, or 128 tokens for the shared
+// 128-row work map written by the routing, or a block of tokens for the shared
 // expert) x one block of output columns.  A work group has 8 waves (two per
 // SIMD).  Per K chunk of 128 (two quantisation groups):
 //   - the activation rows are staged in LDS as bf16, XOR-swizzled by row so
@@ -30,6 +31,14 @@
 //     (up to four) 32-row M-subtiles;
 //   - the weight stream runs several chunks deep in registers so that enough
 //     bytes are outstanding per CU to keep HBM busy.
+//
+// Routed partial outputs are staged in fp16 for the combine.  fp16 keeps 11
+// significant bits but overflows above 65504, so every 32 consecutive
+// columns of an assignment's row are stored as fp16(v * 2^-e) with one
+// exponent e per block, chosen so that the block's largest magnitude lands in
+// [2^14, 2^15): the staging then costs at most 2^-12 of that magnitude for any
+// input range (the exponents are one byte per block, [T][d/32][8] with the
+// slot last, so the combine reads a token's k exponents in one load).
 #include "internal.h"
 
 namespace q4moe {
@@ -43,6 +52,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 4;             // weight chunks held in registers
 constexpr int kALoads = kMT * kSlots / kThreads;
+constexpr int kPartCols = 32;          // columns per staging exponent
 static_assert(kMT * kSlots % kThreads == 0, "A tile split");
 
 template <int N>
@@ -62,31 +72,44 @@ __device__ __forceinline__ int lds_off(int row, int slot) {
     return row * kRowBytes + ((slot ^ (row & 15)) << 4);
 }
 
+// The staging exponent of a block of partial outputs whose largest magnitude
+// is m: m * 2^-e lies in [2^14, 2^15) (below fp16's largest finite value),
+// clamped to [-126, 127] (one signed byte).
+__device__ __forceinline__ int part_exp(float m) {
+    const int e = __builtin_amdgcn_frexp_expf(m) - 15;
+    return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
+// Largest magnitude over the 32 values a lane pair (l, l + 32) holds of one
+// output row in a 32x32 accumulator tile (16 each).
+__device__ __forceinline__ float pair_absmax(const f32x16& acc) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(acc[i]));
+    return fmaxf(m, __shfl_xor(m, 32, 64));
+}
+
+// Byte offset of the staging exponent of assignment a (token a / k, slot
+// a % k) for the 32-column block holding column col.
+__device__ __forceinline__ size_t part_exp_index(const PrefillArgs& a, int asg, int col) {
+    const int t = asg / a.k, s = asg - t * a.k;
+    return ((size_t)t * (a.d / kPartCols) + col / kPartCols) * kMaxTopK + s;
+}
+
 
 // ---------------------------------------------------------------------------
-// Down projections.  Work items [0, sh_items) are the shared expert's 128-token
-// tiles, items [sh_items, sh_items + tile_bound) the routed 128-row work map
-// (entries at or past *n_tiles are empty).  The shared tiles come first so
-// that the fullest items start first.
+// Down projections.  Routed work items are the 128-row work map written by
+// the routing (entries at or past *n_tiles are empty).
 // ---------------------------------------------------------------------------
 struct DownItem {
-    int e, row0, M, shared;
+    int e, row0, M;
 };
 
-__device__ __forceinline__ bool down_item(const PrefillArgs& a, int item, int sh_items, DownItem& it) {
-    if (item < sh_items) {
-        it.e = 0;
-        it.shared = 1;
-        it.row0 = item * kMT;
-        it.M = min(kMT, a.T - it.row0);
-        return true;
-    }
-    item -= sh_items;
+__device__ __forceinline__ bool routed_item(const PrefillArgs& a, int item, DownItem& it) {
     if (item >= *a.n_tiles) return false;
     it.e = a.tile_map[2 * item];
     it.row0 = a.tile_map[2 * item + 1];
     it.M = min(kMT, a.offsets[it.e + 1] - it.row0);
-    it.shared = 0;
     return true;
 }
 
@@ -95,49 +118,92 @@ __device__ __forceinline__ bool down_item(const PrefillArgs& a, int item, int sh
 // l % 32 of its subtile and, in elements 4g..4g+3, the four consecutive
 // weight rows n = 8g + 4h + 0..3 (h = l / 32).  Lanes l and l + 32 hold the
 // same activation row; they trade four-column groups so that each ends with
-// two runs of eight consecutive columns, 16m + 8h .. +7 for m = 0, 1, and
-// stores them whole: fp16 (16 bytes) into the routed outputs `part` (row =
-// assignment), fp32 (32 bytes) into the shared expert's `sh_out` (row =
-// token).  Both lanes of a pair take the same branches (same row).
-__device__ __forceinline__ void down_store(const PrefillArgs& a, int shared, int dst, int wc,
-                                           int half, const f32x16& acc) {
-    if (shared) {
-        float* srow = a.sh_out + (size_t)dst * a.d + wc;
+// two runs of eight consecutive columns, 16m + 8h .. +7 for m = 0, 1.  Both
+// lanes of a pair take the same branches (same row).
+//
+// Routed rows: scaled by the block's staging exponent, stored whole as fp16
+// (16 bytes per run) into `part` (row = assignment dst); lane h = 0 of the
+// pair stores the exponent.
+__device__ __forceinline__ void routed_store(const PrefillArgs& a, int dst, int wc, int half,
+                                             const f32x16& acc) {
+    const int e = part_exp(pair_absmax(acc));
+    if (half == 0) a.pexp[part_exp_index(a, dst, wc)] = (int8_t)e;
+    uint16_t* prow = a.part + (size_t)dst * a.d + wc;
+    auto h16 = [&](float v) { return (uint32_t)f32_to_f16(__builtin_amdgcn_ldexpf(v, -e)); };
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            f32x4 own_lo, own_hi, send;
+    for (int m = 0; m < 2; ++m) {
+        uint2 own_lo, own_hi;
+        own_lo.x = h16(acc[8 * m]) | (h16(acc[8 * m + 1]) << 16);
+        own_lo.y = h16(acc[8 * m + 2]) | (h16(acc[8 * m + 3]) << 16);
+        own_hi.x = h16(acc[8 * m + 4]) | (h16(acc[8 * m + 5]) << 16);
+        own_hi.y = h16(acc[8 * m + 6]) | (h16(acc[8 * m + 7]) << 16);
+        const uint2 send = half ? own_lo : own_hi;
+        uint2 recv;
+        recv.x = (uint32_t)__shfl_xor((int)send.x, 32, 64);
+        recv.y = (uint32_t)__shfl_xor((int)send.y, 32, 64);
+        const uint2 lo = half ? recv : own_lo;
+        const uint2 hi = half ? own_hi : recv;
+        *(u32x4*)(prow + 16 * m + 8 * half) = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+}
+
+// The shared expert's outputs of token tok (a lane pair's row) and the combine:
+// y[tok][c] = bf16( sum_{s<k} w[tok,s] * part[tok*k+s][c] (slot order) +
+// shared[c] ) for the pair's 32 columns from wc.  All k partial loads of a lane
+// are issued before any arithmetic.
+__device__ __forceinline__ void combine_store(const PrefillArgs& a, int tok, int wc, int half,
+                                              const f32x16& acc) {
+    const int k = a.k;
+    float sh[2][8];  // this lane's two runs of 8 columns (16m + 8h .. +7)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                own_lo[i] = acc[4 * (2 * m) + i];      // group 2m (kept by h = 0)
-                own_hi[i] = acc[4 * (2 * m + 1) + i];  // group 2m + 1 (kept by h = 1)
-                send[i] = half ? own_lo[i] : own_hi[i];
+    for (int m = 0; m < 2; ++m) {
+        float own_lo[4], own_hi[4], send[4], recv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            own_lo[i] = acc[4 * (2 * m) + i];      // group 2m (kept by h = 0)
+            own_hi[i] = acc[4 * (2 * m + 1) + i];  // group 2m + 1 (kept by h = 1)
+            send[i] = half ? own_lo[i] : own_hi[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) recv[i] = __shfl_xor(send[i], 32, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sh[m][i] = half ? recv[i] : own_lo[i];
+            sh[m][4 + i] = half ? own_hi[i] : recv[i];
+        }
+    }
+    const uint16_t* prow = a.part + (size_t)tok * k * a.d + wc + 8 * half;
+    u32x4 p[2][kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            p[m][s] = *(const u32x4*)(prow + (size_t)(s < k ? s : 0) * a.d + 16 * m);
+    const uint2 ex = *(const uint2*)(a.pexp + part_exp_index(a, tok * k, wc));
+    float w[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) w[s] = a.topk_w[(size_t)tok * k + (s < k ? s : 0)];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s) {
+            if (s < k) {
+                const int e = (int)(int8_t)(((s < 4 ? ex.x : ex.y) >> (8 * (s & 3))) & 0xFFu);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = __builtin_amdgcn_ldexpf(f16_to_f32(p[m][s][i] & 0xFFFFu), e);
+                    const float hi = __builtin_amdgcn_ldexpf(f16_to_f32(p[m][s][i] >> 16), e);
+                    acc8[2 * i] += w[s] * lo;
+                    acc8[2 * i + 1] += w[s] * hi;
+                }
             }
-            f32x4 recv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) recv[i] = __shfl_xor(send[i], 32, 64);
-            const f32x4 lo = half ? recv : own_lo;
-            const f32x4 hi = half ? own_hi : recv;
-            float* o = srow + 16 * m + 8 * half;
-            *(f32x4*)o = lo;
-            *(f32x4*)(o + 4) = hi;
         }
-    } else {
-        uint16_t* prow = a.part + (size_t)dst * a.d + wc;
+        u32x4 out;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            uint2 own_lo, own_hi;
-            own_lo.x = (uint32_t)f32_to_f16(acc[8 * m]) | ((uint32_t)f32_to_f16(acc[8 * m + 1]) << 16);
-            own_lo.y = (uint32_t)f32_to_f16(acc[8 * m + 2]) | ((uint32_t)f32_to_f16(acc[8 * m + 3]) << 16);
-            own_hi.x = (uint32_t)f32_to_f16(acc[8 * m + 4]) | ((uint32_t)f32_to_f16(acc[8 * m + 5]) << 16);
-            own_hi.y = (uint32_t)f32_to_f16(acc[8 * m + 6]) | ((uint32_t)f32_to_f16(acc[8 * m + 7]) << 16);
-            const uint2 send = half ? own_lo : own_hi;
-            uint2 recv;
-            recv.x = (uint32_t)__shfl_xor((int)send.x, 32, 64);
-            recv.y = (uint32_t)__shfl_xor((int)send.y, 32, 64);
-            const uint2 lo = half ? recv : own_lo;
-            const uint2 hi = half ? own_hi : recv;
-            *(u32x4*)(prow + 16 * m + 8 * half) = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+        for (int i = 0; i < 4; ++i)
+            out[i] = pack_bf16x2(acc8[2 * i] + sh[m][2 * i], acc8[2 * i + 1] + sh[m][2 * i + 1]);
+        *(u32x4*)(a.y + (size_t)tok * a.d + wc + 16 * m + 8 * half) = out;
     }
 }
 
@@ -172,13 +238,18 @@ __device__ __forceinline__ void load_bchunk(const Q4& W, size_t wrow, int K, int
 // Any inter (a multiple of 64): the activation tile streams through LDS one
 // K-chunk at a time, double buffered, one barrier per chunk; each wave owns
 // 32 output columns of a 256-column block.
+//   kShared = false: the routed work map (item = routed 128-row work item);
+//                    outputs go to `part` (routed_store).
+//   kShared = true:  the shared expert over blocks of a.sh_rows tokens (item =
+//                    token block, at most 128 rows); the epilogue combines
+//                    (combine_store) and writes y.
+template <bool kShared>
 __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArgs a,
-                                                                const int sh_items,
                                                                 const int n_items, const int n_cb,
                                                                 const int n_wg) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
     __shared__ int s_src[kMT];  // activation row per tile row (-1: none)
-    __shared__ int s_dst[kMT];  // output row per tile row
+    __shared__ int s_dst[kMT];  // output row per tile row (assignment, or token)
 
     // XCD-aware order: consecutive logical indices (the column blocks of one
     // item, which share the activation rows) stay on one XCD's L2.
@@ -187,17 +258,23 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
     const int item = L / n_cb, cb = L - item * n_cb;
     if (item >= n_items) return;
     DownItem it;
-    if (!down_item(a, item, sh_items, it)) return;
+    if (kShared) {
+        it.e = 0;
+        it.row0 = item * a.sh_rows;
+        it.M = min(a.sh_rows, a.T - it.row0);
+    } else if (!routed_item(a, item, it)) {
+        return;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int K = a.I, Nw = a.d;
-    const uint16_t* A = it.shared ? a.h_sh : a.h;
-    const Q4 W = it.shared ? a.sh_down : a.down;
+    const uint16_t* A = kShared ? a.h_sh : a.h;
+    const Q4 W = kShared ? a.sh_down : a.down;
     if (tid < kMT) {
         int src = -1, dst = -1;
         if (tid < it.M) {
             src = it.row0 + tid;
-            dst = it.shared ? src : a.perm[src];
+            dst = kShared ? src : a.perm[src];
         }
         s_src[tid] = src;
         s_dst[tid] = dst;
@@ -322,7 +399,10 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
     for (int ms = 0; ms < 4; ++ms) {
         const int row = 32 * ms + (lane & 31);
         if (ms >= n_ms || row >= it.M) continue;
-        down_store(a, it.shared, s_dst[row], wcol0, half, acc[ms]);
+        if (kShared)
+            combine_store(a, s_dst[row], wcol0, half, acc[ms]);
+        else
+            routed_store(a, s_dst[row], wcol0, half, acc[ms]);
     }
 }
 
@@ -335,8 +415,8 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
 // whose cost midpoints fall in its 1/G share, so the runs tile the unit list
 // exactly and carry about the same work.
 // ---------------------------------------------------------------------------
-constexpr int kMaxItems =
-    (MOE_MAX_TOKENS + kMT - 1) / kMT + MOE_MAX_TOKENS * kMaxTopK / kMT + kMaxExperts;
+// routed 128-row work items at most (the capacity of the 128-row work map)
+constexpr int kMaxRoutedItems = MOE_MAX_TOKENS * kMaxTopK / kMT + kMaxExperts;
 
 __device__ __forceinline__ int unit_cost(int M) { return 2 + ((M + 31) >> 5); }
 
@@ -346,7 +426,7 @@ __device__ __forceinline__ int unit_cost(int M) { return 2 + ((M + 31) >> 5); }
 template <typename RowsOf>
 __device__ __forceinline__ void cost_prefix(int n_items, int n_cb, int* s_pre, int* s_wtot,
                                             RowsOf&& rows_of) {
-    constexpr int kPer = (kMaxItems + kThreads - 1) / kThreads;
+    constexpr int kPer = (kMaxRoutedItems + kThreads - 1) / kThreads;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = (n_items + kThreads - 1) / kThreads;
     int cost[kPer];
@@ -400,35 +480,30 @@ __device__ __forceinline__ int run_start(int g, int G, int n_items, int n_cb, co
 }
 
 // ---------------------------------------------------------------------------
-// Down projection with the activation tile resident in LDS (inter in
-// (384, 512], four K-chunks), persistent.  A unit is (work item, 256-column
-// block); the units are ordered item by item (shared-expert tiles first) and
-// every work group takes one cost-balanced contiguous run of them.  Consecutive
-// units of a run mostly share their item, so the M x inter bf16 activation
-// tile is loaded into LDS only when the item changes; the weights stream
-// through registers as one continuous pipeline over the whole run (three
-// chunks in flight, across unit boundaries).  Each 256-column block is
-// written as soon as its last chunk is done.
+// Routed down projection with the activation tile resident in LDS (inter in
+// (384, 512], four K-chunks), persistent.  A unit is (routed work item,
+// 256-column block); the units are ordered item by item and every work group
+// takes one cost-balanced contiguous run of them.  Consecutive units of a run
+// mostly share their item, so the M x inter bf16 activation tile is loaded
+// into LDS only when the item changes; the weights stream through registers
+// as one continuous pipeline over the whole run (three chunks in flight,
+// across unit boundaries).  Each 256-column block is written as soon as its
+// last chunk is done.
 // ---------------------------------------------------------------------------
 constexpr int kDnMaxI = 512;
 constexpr int kDnCols = 256;  // output columns per unit: 8 waves x 32
 
-// The down kernel's schedule: items in its order (shared-expert tiles, then the
-// routed work map), their cost prefix over (n_cb 256-column units per item)
-// and their experts (-1: shared), written to the workspace by one work group
-// of the gate/up kernel so that the down kernel's work groups only load it.
+// The down kernel's schedule: the routed items' cost prefix over (n_cb
+// 256-column units per item) and their experts, written to the workspace by
+// one work group of the gate/up kernel so that the down kernel's work groups
+// only load it.
 __device__ __forceinline__ void down_schedule(const PrefillArgs& a, int* s_wtot) {
-    const int sh_items = (a.T + kMT - 1) / kMT;
-    const int n_items = sh_items + *a.n_tiles;
+    const int n_items = *a.n_tiles;
     const int n_cb = (a.d + kDnCols - 1) / kDnCols;
     cost_prefix(n_items, n_cb, a.dn_pre, s_wtot, [&](int i) {
-        // straight-line form of down_item (every load address valid)
-        const bool sh = i < sh_items;
-        const int t = sh ? 0 : i - sh_items;
-        const int e = a.tile_map[2 * t], r0 = a.tile_map[2 * t + 1];
-        const int end = sh ? a.T : a.offsets[e + 1];
-        a.dn_exp[i] = sh ? -1 : e;
-        return min(kMT, end - (sh ? i * kMT : r0));
+        const int e = a.tile_map[2 * i], r0 = a.tile_map[2 * i + 1];
+        a.dn_exp[i] = e;
+        return min(kMT, a.offsets[e + 1] - r0);
     });
 }
 
@@ -438,12 +513,11 @@ __device__ __forceinline__ void down_schedule(const PrefillArgs& a, int* s_wtot)
 // per lane, issued with the codes of the unit's first chunk.
 template <bool kSB4>
 __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillArgs a,
-                                                                 const int sh_items,
                                                                  const int n_cb) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kMT * kDnMaxI * 2];
     __shared__ int s_dst[kMT];
-    __shared__ int s_pre[kMaxItems + 1];  // cost of the units before item i
-    __shared__ short s_exp[kMaxItems];    // expert of item i, -1 for the shared expert
+    __shared__ int s_pre[kMaxRoutedItems + 1];  // cost of the units before item i
+    __shared__ short s_exp[kMaxRoutedItems];    // expert of item i
     // each wave's 32 x 32 fp16 output tile on its way to `part`: row t,
     // 16-byte slot s at t * 64 + 16 * (s ^ ((t >> 1) & 3))
     __shared__ __attribute__((aligned(16))) uint16_t s_out[kWaves][32 * 32];
@@ -451,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int G = gridDim.x, g = blockIdx.x;
     const int K = a.I, Nw = a.d;
-    const int n_items = sh_items + *a.n_tiles;
+    const int n_items = *a.n_tiles;
 
     // ---- this work group's run of units ----
     // the item cost prefix and the items' experts were computed by the
@@ -483,32 +557,28 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     // with kSB4 the unit's scales and biases come with it
     auto load_next_b = [&](BChunk& st, u32x4& s4, u32x4& b4, auto with_sb) {
         const int e = __builtin_amdgcn_readfirstlane(s_exp[w_item]);
-        // field by field (a per-lane select of a whole Q4 would be read from
-        // the kernel arguments through memory)
-        const bool sh = e < 0;
-        const uint32_t* Wq = sh ? a.sh_down.q : a.down.q;
-        const uint16_t* Ws = sh ? a.sh_down.scale : a.down.scale;
-        const uint16_t* Wb = sh ? a.sh_down.bias : a.down.bias;
         const int wc = w_blk * kDnCols + 32 * wave;
-        const size_t wrow = (size_t)(sh ? 0 : e) * Nw + (wc < Nw ? wc + (lane & 31) : 0);
+        const size_t wrow = (size_t)e * Nw + (wc < Nw ? wc + (lane & 31) : 0);
         const int kc0 = w_c * kKC < K ? w_c * kKC : 0;
         const int kc1 = kc0 + kGroup < K ? kc0 + kGroup : kc0;
-        const uint32_t* qrow = Wq + wrow * (K / 8) + 4 * half;
+        const uint32_t* qrow = a.down.q + wrow * (K / 8) + 4 * half;
         st.lo = *(const u32x4*)(qrow + kc0 / 8);
         st.hi = *(const u32x4*)(qrow + kc1 / 8);
         if (kSB4) {
             if (decltype(with_sb)::value) {
-                s4 = *(const u32x4*)(Ws + wrow * (K / kGroup));
-                b4 = *(const u32x4*)(Wb + wrow * (K / kGroup));
+                s4 = *(const u32x4*)(a.down.scale + wrow * (K / kGroup));
+                b4 = *(const u32x4*)(a.down.bias + wrow * (K / kGroup));
             }
         } else {
             const size_t grow = wrow * (K / kGroup);
             if (pair_sb) {
-                st.sp = *(const uint32_t*)(Ws + grow + kc0 / kGroup);
-                st.bp = *(const uint32_t*)(Wb + grow + kc0 / kGroup);
+                st.sp = *(const uint32_t*)(a.down.scale + grow + kc0 / kGroup);
+                st.bp = *(const uint32_t*)(a.down.bias + grow + kc0 / kGroup);
             } else {
-                st.sp = (uint32_t)Ws[grow + kc0 / kGroup] | ((uint32_t)Ws[grow + kc1 / kGroup] << 16);
-                st.bp = (uint32_t)Wb[grow + kc0 / kGroup] | ((uint32_t)Wb[grow + kc1 / kGroup] << 16);
+                st.sp = (uint32_t)a.down.scale[grow + kc0 / kGroup] |
+                        ((uint32_t)a.down.scale[grow + kc1 / kGroup] << 16);
+                st.bp = (uint32_t)a.down.bias[grow + kc0 / kGroup] |
+                        ((uint32_t)a.down.bias[grow + kc1 / kGroup] << 16);
             }
         }
         if (!w_end && ++w_c == nk) {
@@ -541,14 +611,12 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
     // weight times a finite value must stay zero).
     DownItem it;
     auto load_tile = [&](int item) {
-        down_item(a, item, sh_items, it);
+        routed_item(a, item, it);
         // tid laundered here, so that the per-lane tile offsets are computed
         // per load instead of being hoisted out of the unit loop (and spilled)
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
-        const uint16_t* A = it.shared ? a.h_sh : a.h;
-        if (tid < kMT)
-            s_dst[tid] = tid < it.M ? (it.shared ? it.row0 + tid : a.perm[it.row0 + tid]) : -1;
+        if (tid < kMT) s_dst[tid] = tid < it.M ? a.perm[it.row0 + tid] : -1;
         constexpr int slots = nk * kSlots;  // 16-byte slots per row (K padded to the chunk)
         constexpr int per = kMT * slots / kThreads;
         static_assert(kMT * slots % kThreads == 0, "resident tile split");
@@ -559,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
             const int row = i / slots, slot = i - row * slots;
             const int kcol = 8 * slot;
             const size_t off = (size_t)(it.row0 + (row < it.M ? row : 0)) * K + (kcol < K ? kcol : 0);
-            v[p] = *(const u32x4*)(A + off);
+            v[p] = *(const u32x4*)(a.h + off);
         }
 #pragma unroll
         for (int p = 0; p < per; ++p) {
@@ -625,36 +693,33 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
             b4c = b4n;
         }
         if (wc < Nw) {
-            if (it.shared) {
+            // through the wave's LDS tile, so that a store instruction writes
+            // 16 rows x 64 contiguous bytes; every row of the tile is scaled by
+            // its staging exponent first (a lane pair holds one row)
+            unsigned char* so = (unsigned char*)s_out[wave];
+            const int t = lane & 31;
 #pragma unroll
-                for (int ms = 0; ms < NMS; ++ms) {
-                    const int row = 32 * ms + (lane & 31);
-                    if (row < it.M) down_store(a, 1, s_dst[row], wc, half, acc[ms]);
+            for (int ms = 0; ms < NMS; ++ms) {
+                const int e = part_exp(pair_absmax(acc[ms]));
+                const int row_e = 32 * ms + t;
+                if (half == 0 && row_e < it.M) a.pexp[part_exp_index(a, s_dst[row_e], wc)] = (int8_t)e;
+                auto h16 = [&](float v) {
+                    return (uint32_t)f32_to_f16(__builtin_amdgcn_ldexpf(v, -e));
+                };
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {  // columns 8gq + 4h .. +3: 8-byte unit 2gq + h
+                    uint2 v;
+                    v.x = h16(acc[ms][4 * gq]) | (h16(acc[ms][4 * gq + 1]) << 16);
+                    v.y = h16(acc[ms][4 * gq + 2]) | (h16(acc[ms][4 * gq + 3]) << 16);
+                    const int slot = gq ^ ((t >> 1) & 3);
+                    *(uint2*)(so + t * 64 + 16 * slot + 8 * half) = v;
                 }
-            } else {
-                // routed rows: through the wave's LDS tile, so that a store
-                // instruction writes 16 rows x 64 contiguous bytes
-                unsigned char* so = (unsigned char*)s_out[wave];
-                const int t = lane & 31;
 #pragma unroll
-                for (int ms = 0; ms < NMS; ++ms) {
-#pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {  // columns 8gq + 4h .. +3: 8-byte unit 2gq + h
-                        uint2 v;
-                        v.x = (uint32_t)f32_to_f16(acc[ms][4 * gq]) |
-                              ((uint32_t)f32_to_f16(acc[ms][4 * gq + 1]) << 16);
-                        v.y = (uint32_t)f32_to_f16(acc[ms][4 * gq + 2]) |
-                              ((uint32_t)f32_to_f16(acc[ms][4 * gq + 3]) << 16);
-                        const int slot = gq ^ ((t >> 1) & 3);
-                        *(uint2*)(so + t * 64 + 16 * slot + 8 * half) = v;
-                    }
-#pragma unroll
-                    for (int pass = 0; pass < 2; ++pass) {
-                        const int r = 16 * pass + (lane >> 2), sg = lane & 3;
-                        const u32x4 v = *(const u32x4*)(so + r * 64 + 16 * (sg ^ ((r >> 1) & 3)));
-                        const int row = 32 * ms + r;
-                        if (row < it.M) *(u32x4*)(a.part + (size_t)s_dst[row] * a.d + wc + 8 * sg) = v;
-                    }
+                for (int pass = 0; pass < 2; ++pass) {
+                    const int r = 16 * pass + (lane >> 2), sg = lane & 3;
+                    const u32x4 v = *(const u32x4*)(so + r * 64 + 16 * (sg ^ ((r >> 1) & 3)));
+                    const int row = 32 * ms + r;
+                    if (row < it.M) *(u32x4*)(a.part + (size_t)s_dst[row] * a.d + wc + 8 * sg) = v;
                 }
             }
         }
@@ -759,6 +824,10 @@ struct WChunk {
     uint32_t sp, bp;
 };
 
+// items of the gate/up kernel at most: the routed work map plus the shared
+// expert's blocks of kGuShRows tokens
+constexpr int kGuMaxItems = kMaxRoutedItems + (MOE_MAX_TOKENS + kGuShRows - 1) / kGuShRows;
+
 // The items of group q of Q (item = routed tile, then the shared expert's row
 // blocks), written to s_items[0, n_run) in the order the group runs them.
 // The items are ordered by subtile count, largest first (stable inside a
@@ -770,7 +839,7 @@ struct WChunk {
 // four subtile counts, so every item's position and cost prefix have a closed
 // form in the class totals and its rank inside its class; every work group
 // computes only its own run.  Uniform results; contains barriers.
-constexpr int kGuPer = (kMaxItems + kGuThreads - 1) / kGuThreads;
+constexpr int kGuPer = (kGuMaxItems + kGuThreads - 1) / kGuThreads;
 // estimated cost of a gate/up unit with `ms` 32-row subtiles
 __device__ __forceinline__ int gu_unit_cost(int ms) { return 2 + ms; }
 constexpr int kGuRunMax = 512;  // items one group may hold (s_items)
@@ -1296,11 +1365,10 @@ static int device_cus() {
     return cus[dev];
 }
 
-// Whether the down projection runs as down_resident_kernel, whose schedule
-// the gate/up kernel writes.
+// Whether the routed down projection runs as down_resident_kernel, whose
+// schedule the gate/up kernel writes.
 static bool down_is_resident(const PrefillArgs& a) {
-    const int n_items = (a.T + kMT - 1) / kMT + a.tile_bound;
-    return (a.I + kKC - 1) / kKC == kStages && n_items <= kMaxItems;
+    return (a.I + kKC - 1) / kKC == kStages && a.tile_bound <= kMaxRoutedItems;
 }
 
 static hipError_t launch_gate_up(const PrefillArgs& a_in, hipStream_t s) {
@@ -1319,72 +1387,48 @@ static hipError_t launch_gate_up(const PrefillArgs& a_in, hipStream_t s) {
     return hipGetLastError();
 }
 
-static hipError_t launch_down(const PrefillArgs& a, hipStream_t s) {
-    const int sh_items = (a.T + kMT - 1) / kMT;
-    const int n_items = sh_items + a.tile_bound;
-    if ((a.I + kKC - 1) / kKC == kStages) {
-        if (n_items > kMaxItems || !a.dn_pre || !a.dn_exp) return hipErrorInvalidValue;
-        const int n_cb = (a.d + kDnCols - 1) / kDnCols;
-        const int grid = min(device_cus(), n_items * n_cb);
+// The routed rows' down projection into the fp16 staging rows.
+static hipError_t launch_down_routed(const PrefillArgs& a, hipStream_t s) {
+    const int n_cb = (a.d + kDnCols - 1) / kDnCols;
+    if (down_is_resident(a)) {
+        if (!a.dn_pre || !a.dn_exp) return hipErrorInvalidValue;
+        const int grid = min(device_cus(), a.tile_bound * n_cb);
         if (a.I % (8 * kGroup) == 0)
-            hipLaunchKernelGGL(down_resident_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a,
-                               sh_items, n_cb);
+            hipLaunchKernelGGL(down_resident_kernel<true>, dim3(grid), dim3(kThreads), 0, s, a, n_cb);
         else
-            hipLaunchKernelGGL(down_resident_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a,
-                               sh_items, n_cb);
+            hipLaunchKernelGGL(down_resident_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a, n_cb);
     } else {
-        const int n_cb = (a.d + 255) / 256;
-        const int n_wg = ((n_items * n_cb) + 7) & ~7;
-        hipLaunchKernelGGL(down_chunked_kernel, dim3(n_wg), dim3(kThreads), 0, s, a, sh_items,
-                           n_items, n_cb, n_wg);
+        const int n_wg = ((a.tile_bound * n_cb) + 7) & ~7;
+        hipLaunchKernelGGL(down_chunked_kernel<false>, dim3(n_wg), dim3(kThreads), 0, s, a,
+                           a.tile_bound, n_cb, n_wg);
     }
     trace_point(s);
     return hipGetLastError();
 }
 
-// y_t = bf16( sum_{s<k} w[t,s] * part[t*k+s] + sh_out[t] ): the k routed
-// outputs in slot order, then the shared expert, all in fp32.  One work group
-// per token; each thread owns 8 consecutive columns, so every load is 16 or 32
-// contiguous bytes per lane and a wave reads whole 1 KB spans.
-__global__ __launch_bounds__(256) void combine_kernel(const PrefillArgs a) {
-    const int t = blockIdx.x, d = a.d, k = a.k;
-    float w[kMaxTopK];
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) w[s] = a.topk_w[(size_t)t * k + (s < k ? s : 0)];
-    const uint16_t* pt = a.part + (size_t)t * k * d;
-    const float* st = a.sh_out + (size_t)t * d;
-    for (int c = 8 * (int)threadIdx.x; c < d; c += 8 * 256) {
-        u32x4 p[kMaxTopK];
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) p[s] = *(const u32x4*)(pt + (size_t)(s < k ? s : 0) * d + c);
-        const f32x4 sh0 = *(const f32x4*)(st + c);
-        const f32x4 sh1 = *(const f32x4*)(st + c + 4);
-        float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (s < k) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[2 * i] += w[s] * f16_to_f32(p[s][i] & 0xFFFFu);
-                    acc[2 * i + 1] += w[s] * f16_to_f32(p[s][i] >> 16);
-                }
-            }
-        }
-        u32x4 out;
-        out[0] = pack_bf16x2(acc[0] + sh0[0], acc[1] + sh0[1]);
-        out[1] = pack_bf16x2(acc[2] + sh0[2], acc[3] + sh0[3]);
-        out[2] = pack_bf16x2(acc[4] + sh1[0], acc[5] + sh1[1]);
-        out[3] = pack_bf16x2(acc[6] + sh1[2], acc[7] + sh1[3]);
-        *(u32x4*)(a.y + (size_t)t * d + c) = out;
-    }
+// Rows per shared-expert down item: the tallest of 128, 64, 32 that still
+// gives every CU a work group (at least twice over for 128), so the combine's
+// reads of the staged rows are spread over the whole chip.
+static int shared_down_rows(int T, int n_cb) {
+    const int cus = device_cus();
+    if ((T + 127) / 128 * n_cb >= 2 * cus) return 128;
+    if ((T + 63) / 64 * n_cb >= cus) return 64;
+    return 32;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-    hipError_t err = launch_gate_up(a, s);
+hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t s) {
+    hipError_t err = launch_gate_up(a_in, s);
     if (err != hipSuccess) return err;
-    err = launch_down(a, s);
+    err = launch_down_routed(a_in, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(256), 0, s, a);
+    // the shared expert's down projection with the combine in its epilogue
+    PrefillArgs a = a_in;
+    const int n_cb = (a.d + 255) / 256;
+    a.sh_rows = shared_down_rows(a.T, n_cb);
+    const int n_items = (a.T + a.sh_rows - 1) / a.sh_rows;
+    const int n_wg = ((n_items * n_cb) + 7) & ~7;
+    hipLaunchKernelGGL(down_chunked_kernel<true>, dim3(n_wg), dim3(kThreads), 0, s, a, n_items,
+                       n_cb, n_wg);
     trace_point(s);
     return hipGetLastError();
 }

@@ -144,8 +144,9 @@ def test_workspace_bytes_cover_the_staged_buffers():
     for T, d, I, E, k in ((2048, 2048, 512, 256, 8), (32, 512, 128, 32, 4), (1, 2048, 512, 256, 8)):
         L = _layer(d, I, E, k)  # keep the struct alive across the call
         n = lib.moe_workspace_bytes(C.addressof(L), T)
-        # h, shared h, fp16 routed outputs, fp32 shared outputs
-        staged = 2 * (T * k * I + T * I + T * k * d) + 4 * T * d
+        # h, shared h, fp16 routed outputs, their exponents (one byte per 32
+        # columns of a token, slots padded to MOE_MAX_TOPK)
+        staged = 2 * (T * k * I + T * I + T * k * d) + T * (d // 32) * _abi.MOE_MAX_TOPK
         # decode region for up to MOE_MAX_DECODE_TOKENS tokens: router partial
         # sums, logits, h of the k + 1 experts per token
         nt = _abi.MOE_MAX_DECODE_TOKENS
@@ -153,6 +154,26 @@ def test_workspace_bytes_cover_the_staged_buffers():
         assert staged + dec <= n <= staged + dec + 64 * 1024
     bad = _layer(d=100)
     assert lib.moe_workspace_bytes(C.addressof(bad), 16) == 0
+
+
+def test_router_loads_stay_inside_their_k_slice():
+    # The router kernel's waves each take one eighth of d; a lane of wave w
+    # reads 8 consecutive k from kk at every padded K-step.  For every d the
+    # ABI accepts, every read [kk, kk + 8) lies in [w*d/8, (w+1)*d/8) (so it
+    # stays inside x and W_r), and every in-range step reads where it computes.
+    S, waves = 4, 8
+    for d in range(64, _abi.MOE_MAX_D + 1, 64):
+        kq = d // waves
+        n_steps = -(-(kq // 16 + (kq % 16 != 0)) // S) * S
+        for w in range(waves):
+            kbeg, kend = w * kq, (w + 1) * kq
+            for step in range(n_steps + S - 1):  # the loads run S - 1 steps ahead
+                k = kbeg + 16 * step
+                for half in (0, 1):
+                    kk = k + 8 * half if k + 8 * half + 8 <= kend else kbeg
+                    assert kbeg <= kk and kk + 8 <= kend, (d, w, step, half)
+                    if k + 8 * half < kend:
+                        assert kk == k + 8 * half
 
 
 def test_block_map_capacity_bounds_the_tile_count():
