@@ -5,10 +5,18 @@ Bars:
     block maps: bit-exact, routing done from the oracle's fp32 logits;
   - router logits: max |err| <= 1e-3 * RMS(oracle logits);
   - renormalised scores: |err| <= 2e-6 (fp32 against the oracle's fp64);
-  - layer outputs (bf16): max |y - y_exact| <= 2e-2 * RMS(y_exact), y_exact the
-    oracle's unrounded fp64 sum; run-to-run bit-identical.
-Full-size workloads are checked on sampled tokens (the oracle computes each
-output token independently); small shapes on every token.
+  - layer outputs (bf16): every element within 2e-2 * RMS(y_exact) of y_exact,
+    the oracle's unrounded fp64 sum -- or, where rounding to bf16 alone can
+    cost more than that (an output beyond about 5 RMS), within half a bf16
+    ulp of y_exact plus 2e-3 * RMS (the fp32 sum-order noise that can move a
+    value across a rounding midpoint); run-to-run bit-identical.
+Full-size workloads are checked on the tokens of the first and last sorted
+row of every 128-row work item of the grouped GEMMs and of every 32-token
+block (the oracle computes each output token independently), so every work
+item of every kernel is reached; small shapes on every token.  Routing on the
+GPU's own logits must pick the oracle's expert set for every token whose k-th
+and (k+1)-th oracle logits are further apart than twice the measured logit
+error.
 """
 import numpy as np
 import pytest
@@ -22,6 +30,7 @@ from workloads import (WORKLOADS, bits_to_f32, decode_inputs, make_layer, random
 pytestmark = pytest.mark.gpu
 
 Y_TOL = 2e-2
+Y_MIDPOINT_SLACK = 2e-3
 LOGIT_TOL = 1e-3
 W_TOL = 2e-6
 
@@ -45,10 +54,20 @@ def host_bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def bf16_half_ulp(v):
+    """Half the spacing of bf16 numbers at |v| (8 significant bits; 0 at 0)."""
+    _, e = np.frexp(np.abs(v))  # |v| in [2^(e-1), 2^e)
+    return np.where(v == 0, 0.0, np.ldexp(1.0, e - 9))
+
+
 def y_error(y_bits, y_exact):
+    """(max |err| / RMS, RMS, worst err / allowed): allowed per element is
+    max(Y_TOL * RMS, half a bf16 ulp of y_exact + Y_MIDPOINT_SLACK * RMS); the
+    output passes when the last value is <= 1."""
     err = np.abs(bits_to_f32(y_bits).astype(np.float64) - y_exact)
     rms = float(np.sqrt(np.mean(y_exact ** 2)))
-    return float(err.max()) / rms, rms
+    allowed = np.maximum(Y_TOL * rms, bf16_half_ulp(y_exact) + Y_MIDPOINT_SLACK * rms)
+    return float(err.max()) / rms, rms, float((err / allowed).max())
 
 
 def compare_routing(r, ref, T, E, k, bm_ref, tm_ref):
@@ -72,14 +91,52 @@ def oracle_routing(logits, k):
     return ref, bm, tm
 
 
-def sample_tokens(T, seed, n=12):
-    rng = np.random.default_rng(seed)
-    pick = {0, 1, T // 2, T - 2, T - 1} | set(rng.integers(0, T, n).tolist())
-    return np.array(sorted(t for t in pick if 0 <= t < T), np.int32)
+def item_tokens(ref, T, k, items=None, seed=0):
+    """Tokens of the first and last sorted row of every 128-row work item (or of
+    `items` of them, drawn with `seed`, always including the first and the last
+    items), plus the first and last token of every 32-token block (64-token
+    above T = 16384, where the shared expert's items are 64 or 128 tokens):
+    every work item of the grouped GEMMs and of the shared expert's GEMMs then
+    has a compared output row."""
+    tm, n = oracle.block_map(ref["counts"], ref["offsets"], q4.TILE_ROWS)
+    sel = np.arange(n)
+    if items is not None and items < n:
+        rng = np.random.default_rng(seed)
+        sel = np.unique(np.concatenate([[0, n - 1], rng.choice(n, items, replace=False)]))
+    pick = set()
+    for i in sel:
+        e, r0 = int(tm[i, 0]), int(tm[i, 1])
+        last = min(r0 + q4.TILE_ROWS, int(ref["offsets"][e + 1])) - 1
+        pick.add(int(ref["perm"][r0]) // k)
+        pick.add(int(ref["perm"][last]) // k)
+    blk = 32 if T <= 16384 else 64
+    for b in range(0, T, blk):
+        pick.update((b, min(b + blk - 1, T - 1)))
+    return np.array(sorted(pick), np.int32)
 
 
-def run_layer_case(L, x, dev, tokens=None, name=""):
-    """Route on the GPU from the oracle's logits, run prefill, compare."""
+def check_own_routing(l_gpu, l_ref, own_idx, ref_idx, k):
+    """Tokens whose expert set from the GPU's own logits differs from the
+    oracle's; every such token must have its k-th and (k+1)-th oracle logits
+    within twice the largest logit error of each other (a near tie)."""
+    differ = (np.sort(own_idx, 1) != np.sort(ref_idx, 1)).any(1)
+    E = l_ref.shape[1]
+    if k < E:
+        srt = -np.sort(-l_ref.astype(np.float64), axis=1)
+        gap = srt[:, k - 1] - srt[:, k]
+        bound = 2.0 * float(np.abs(l_gpu.astype(np.float64) - l_ref).max())
+        assert not (differ & (gap > bound)).any(), \
+            f"expert sets differ on tokens {np.where(differ & (gap > bound))[0][:8]} " \
+            f"whose k-th logit gap exceeds {bound:.2e}"
+    else:
+        assert not differ.any()
+    return int(differ.sum())
+
+
+def run_layer_case(L, x, dev, tokens=None, name="", items=None):
+    """Route on the GPU from the oracle's logits, run prefill, compare.
+    tokens: None (every token), "items" (item_tokens, at most `items` work
+    items) or an array of token indices."""
     T, E, k = x.shape[0], L["n_experts"], L["top_k"]
     layer = q4.DeviceLayer.from_host(L, dev)
     xd = xdev(x, dev)
@@ -97,7 +154,7 @@ def run_layer_case(L, x, dev, tokens=None, name=""):
     r.logits.copy_(torch.from_numpy(l_ref))
     q4.route(layer, xd, routing=r, logits_in=True)
     compare_routing(r, ref, T, E, k, bm, tm)
-    differ = int((np.sort(own_idx, 1) != np.sort(ref["idx"], 1)).any(1).sum())
+    differ = check_own_routing(l_gpu, l_ref, own_idx, ref["idx"], k)
     ws = q4.workspace(layer, T, dev)
     y = q4.prefill(layer, xd, r, ws)
     y2 = q4.prefill(layer, xd, r, ws)
@@ -106,13 +163,15 @@ def run_layer_case(L, x, dev, tokens=None, name=""):
     assert np.array_equal(yb, yb2), "prefill is not run-to-run deterministic"
     if tokens is None:
         tokens = np.arange(T, dtype=np.int32)
+    elif isinstance(tokens, str):
+        tokens = item_tokens(ref, T, k, items)
     y_exact, _ = oracle.layer_tokens(L, x, tokens, ref["idx"], ref["w"])
-    err, rms = y_error(yb[tokens], y_exact)
+    err, rms, worst = y_error(yb[tokens], y_exact)
     log(f"{name} T={T} E={E} k={k}: logits err/rms={lerr:.2e}, tokens whose expert set "
-        f"differs on GPU logits={differ}, y max err/rms={err:.3e} (rms {rms:.3f}, "
-        f"{len(tokens)} tokens)")
+        f"differs on GPU logits={differ}, y max err/rms={err:.3e}, worst err/allowed="
+        f"{worst:.3f} (rms {rms:.3f}, {len(tokens)} tokens)")
     assert lerr <= LOGIT_TOL
-    assert err <= Y_TOL
+    assert worst <= 1.0
     return err
 
 
@@ -150,17 +209,11 @@ def test_dequant_bit_exact(dev):
 
 @pytest.mark.parametrize("name", ["tiny", "prefill512", "prefill2048", "skew4096"])
 def test_workload_layer(name, dev):
+    # every work item of the grouped GEMMs reached: the first and last rows of
+    # each 128-row item of the hottest and of the rarest experts alike
     w = WORKLOADS[name]
     L, x = make_layer(w)
-    tokens = None if w.T <= 64 else sample_tokens(w.T, w.seed)
-    if name == "skew4096":  # include tokens of the hottest and of the rarest experts
-        l_ref = oracle.router_logits(x, L["w_router"], L["router_bias"])
-        ref = oracle.route(l_ref, w.top_k)
-        c = ref["counts"]
-        rare = np.where((c > 0) & (c <= 4))[0]
-        extra = [ref["perm"][ref["offsets"][e]] // w.top_k for e in rare[:4]]
-        tokens = np.array(sorted(set(tokens.tolist()) | set(int(t) for t in extra)), np.int32)
-    run_layer_case(L, x, dev, tokens, name)
+    run_layer_case(L, x, dev, None if w.T <= 64 else "items", name)
 
 
 def test_decode_workload(dev):
@@ -187,13 +240,13 @@ def test_decode_workload(dev):
             torch.cuda.synchronize()
             assert np.array_equal(r.topk_idx.cpu().numpy(), ref_all["idx"])
             assert np.abs(r.topk_w.cpu().numpy() - ref_all["w"]).max() <= W_TOL
-            err, rms = y_error(host_bits(y), ref_all["y_exact"])
-            err_own, _ = y_error(host_bits(y_own), ref_all["y_exact"])
+            err, rms, worst = y_error(host_bits(y), ref_all["y_exact"])
+            err_own, _, _ = y_error(host_bits(y_own), ref_all["y_exact"])
             assert np.array_equal(host_bits(y), host_bits(y_again))
             log(f"decode layer {layer_i} step {st}: logits err/rms={lerr:.2e}, y err/rms="
                 f"{err:.3e} (own routing {err_own:.3e}), rms {rms:.3f}")
             assert lerr <= LOGIT_TOL
-            assert err <= Y_TOL
+            assert worst <= 1.0
 
 
 def _decode_tokens_case(L, xs, dev, name):
@@ -225,10 +278,10 @@ def _decode_tokens_case(L, xs, dev, name):
     torch.cuda.synchronize()
     assert np.array_equal(r.topk_idx.cpu().numpy(), ref["idx"])
     assert np.abs(r.topk_w.cpu().numpy() - ref["w"]).max() <= W_TOL
-    err, rms = y_error(host_bits(y2), ref["y_exact"])
+    err, rms, worst = y_error(host_bits(y2), ref["y_exact"])
     log(f"decode_tokens {name} T={T}: logits err/rms={lerr:.2e}, y err/rms={err:.3e}, rms {rms:.3f}")
     assert lerr <= LOGIT_TOL
-    assert err <= Y_TOL
+    assert worst <= 1.0
 
 
 def test_decode_tokens_workload(dev):
@@ -264,6 +317,10 @@ EDGE = [
     (100, 512, 576, 8, 2, False, 8),      # inter > 512 and not a multiple of 512: chunked down GEMM
     (70, 1024, 2048, 8, 2, True, 9),      # the largest inter (chunked down GEMM)
     (40, 8192, 128, 8, 2, False, 10),     # the largest d
+    (300, 512, 512, 16, 4, True, 11),     # inter = 512: the resident down GEMM with one scale
+                                          # load per unit, several items per expert, ragged tails
+    (300, 512, 448, 16, 4, True, 12),     # inter = 448: the resident down GEMM, odd group count
+    (257, 64, 512, 8, 3, False, 13),      # the smallest d (router with one K-step per wave)
 ]
 
 
@@ -273,6 +330,52 @@ def test_edge_shapes(T, d, inter, E, k, bias, seed, dev):
     L = random_layer(rng, d, inter, E, k, router_bias=bias)
     x = random_x(rng, T, d)
     run_layer_case(L, x, dev, None, f"edge{seed}")
+
+
+def test_gate_up_round_robin_schedule(dev):
+    # more gate/up work items than the grouped schedule takes at inter = 2048
+    # (16 column blocks per item): the kernel falls back to its round-robin
+    # unit list; the routed down projection runs chunked
+    rng = np.random.default_rng(1013)
+    T, d, inter, E, k = 30000, 64, 2048, 32, 8
+    L = random_layer(rng, d, inter, E, k)
+    x = random_x(rng, T, d)
+    ref = oracle.route(oracle.router_logits(x, L["w_router"]), k)
+    n_tiles = oracle.block_map(ref["counts"], ref["offsets"], q4.TILE_ROWS)[1]
+    n_items = n_tiles + (T + 63) // 64
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_cb = inter // 128
+    grouped_bound = 512 * 8 * ((cus // 8) // n_cb) // 4
+    assert n_items > grouped_bound, (n_items, grouped_bound)
+    run_layer_case(L, x, dev, "items", "round-robin gate/up", items=300)
+
+
+def test_prefill_at_the_token_limit(dev):
+    # T = 32768 (the limit): more gate/up items than one thread of the
+    # schedule's 512 covers five at a time; every work item compared
+    rng = np.random.default_rng(1014)
+    T, d, inter, E, k = 32768, 64, 512, 256, 8
+    L = random_layer(rng, d, inter, E, k, router_bias=True)
+    x = random_x(rng, T, d)
+    run_layer_case(L, x, dev, "items", "T=32768")
+
+
+def test_large_magnitudes(dev):
+    # x scaled by 1024 (exact in bf16): the routed experts' outputs reach far
+    # past fp16's largest finite value (65504); the staged partials must keep
+    # them
+    rng = np.random.default_rng(1015)
+    T, d, inter, E, k = 96, 512, 128, 32, 4
+    L = random_layer(rng, d, inter, E, k)
+    x = bits_to_f32(random_x(rng, T, d)) * np.float32(1024.0)
+    from workloads import bf16_bits
+    x = bf16_bits(x)
+    r = oracle.route(oracle.router_logits(x, L["w_router"]), k)
+    big = max(float(np.abs(oracle.expert(L, int(r["idx"][t, 0]), x[t])[1]).max())
+              for t in range(4))
+    assert big > 65504.0 * 4, big
+    err = run_layer_case(L, x, dev, None, "x * 1024")
+    log(f"large magnitudes: largest routed output {big:.3e}, y err/rms {err:.3e}")
 
 
 def test_all_tokens_pick_the_same_experts(dev):
@@ -337,9 +440,9 @@ def test_small_decode_shapes(dev):
         y = q4.decode(layer, xdev(x, dev), ws, routing=r, logits_in=True)
         torch.cuda.synchronize()
         assert np.array_equal(r.topk_idx.cpu().numpy(), ref["idx"])
-        err, _ = y_error(host_bits(y), ref["y_exact"])
+        err, _, worst = y_error(host_bits(y), ref["y_exact"])
         log(f"decode d={d} I={inter} E={E} k={k}: y err/rms={err:.3e}")
-        assert err <= Y_TOL
+        assert worst <= 1.0
 
 
 # ------------------------------------------------------------------ graph capture

@@ -366,6 +366,24 @@ def test_outputs_are_bf16_of_the_exact_sum():
     assert np.mean(out["y"] == _torch_bf16(ye)) > 0.999
 
 
+def test_output_bar_half_ulp_is_the_bf16_rounding_bound():
+    # The GPU parity bar lets an output element be off by half a bf16 ulp of
+    # the exact value (+ a small slack) where that exceeds 2e-2 * RMS.  The
+    # helper's half ulp must bound the correct rounding's error everywhere and
+    # be attained at midpoints: checked against the oracle's rounding.
+    import test_gpu_parity as tgp
+    rng = np.random.default_rng(26)
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))
+    err = np.abs(bits_to_f32(oracle.bf16_round(v)).astype(np.float64) - v)
+    assert (err <= tgp.bf16_half_ulp(v)).all()
+    # midpoints between consecutive bf16 numbers: the error is exactly half an ulp
+    lo = bits_to_f32(np.arange(0x3F80, 0x3FFF, dtype=np.uint16)).astype(np.float64)
+    mid = (lo + bits_to_f32(np.arange(0x3F81, 0x4000, dtype=np.uint16))) / 2
+    err = np.abs(bits_to_f32(oracle.bf16_round(mid)).astype(np.float64) - mid)
+    assert np.array_equal(err, tgp.bf16_half_ulp(mid))
+    assert tgp.bf16_half_ulp(np.array([0.0]))[0] == 0.0
+
+
 def test_tiny_workload_layer_runs_and_is_deterministic():
     w = WORKLOADS["tiny"]
     L, x = make_layer(w)
