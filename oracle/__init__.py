@@ -178,8 +178,9 @@ def layer(L: dict, x, logits=None, tokens=None):
 
 
 # ---- greedy decoding's token hand-off (page section "Decode: minimize bytes
-# per token": the GPU picks the argmax and writes the token ID into the next
-# step's input slot).  The head and the embedding table are V x d Q4 matrices.
+# per token": the chosen token stays on the device, from the largest output
+# logit into the following step's input).  The head and the embedding table
+# are V x d Q4 matrices.
 
 def lm_logits(x, q, scale, bias) -> np.ndarray:
     """fp32 [V] logits of a [V, d] Q4 matrix (q: uint32 [V, d/8]) applied to x (bf16 [d])."""

@@ -10,19 +10,17 @@
  * Sources.  [Lily-M5] is the page "Perplexity's Lily beats MLX-LM on MacBook
  * M5 because it only runs one model"; sections are named in quotes.
  *   [Lily-M5, "Why Qwen3.6-35B-A3B is a weird workload"]
- *       a router scores the experts, picks 8, and one shared expert sees
- *       every token.
- *   [Lily-M5, "Prefill: keep routing on the GPU, dequantize in flight"]
- *       groupwise affine 4-bit weights, every group of 64 weights sharing a
- *       bf16 scale and a bf16 bias; the tensor ops take bf16 operands, so the
- *       weights are reconstructed (as bf16) before the multiply; the grouped
- *       GEMM accumulates in FP32 and writes bf16; grouping needs histogram,
- *       prefix scan, scatter and block map after every top-k selection; tiles
- *       of 32 rows.
- *   [Lily-M5, "Decode: minimize bytes per token"]
- *       expert input projections fused with the gate activation, expert
- *       output projection fused with the routing scores and the shared
+ *       8 of 256 routed experts per token, plus 1 always-on shared
  *       expert.
+ *   [Lily-M5, "Prefill: keep routing on the GPU, dequantize in flight"]
+ *       4-bit codes, one bf16 scale and one bf16 bias per group of 64; the
+ *       matrix units consume bf16, so each weight is rebuilt as a bf16 value
+ *       before it is multiplied; FP32 sums, bf16 results; after each top-k
+ *       step the rows are grouped per expert (histogram, prefix scan,
+ *       scatter, block map); 32-row tiles.
+ *   [Lily-M5, "Decode: minimize bytes per token"]
+ *       the gate activation is folded into the input projections, and the
+ *       scores and the shared expert into the output projection.
  *
  * Readings where the pages leave a step open (the plainest one the rest of
  * the text supports):
@@ -306,9 +304,9 @@ void oracle_bf16_round(const double* v, int64_t n, uint16_t* out) {
 }
 
 /* ---- O13-O15: greedy decoding's token hand-off --------------------------- */
-/* [Lily-M5, "Decode: minimize bytes per token"]: the token never goes back to
-   the CPU between decode steps; the GPU takes the argmax over the output
-   logits and puts the token ID straight into the input slot of the next step.
+/* [Lily-M5, "Decode: minimize bytes per token"]: the greedy token stays on the
+   device between decode steps; the largest output logit selects it and it
+   feeds the following step's input directly.
    Readings (the pages give no further detail):
      - the output projection ("LM head") and the input embedding table are V x d
        matrices in the experts' group-64 Q4 format, used as bf16 weights;

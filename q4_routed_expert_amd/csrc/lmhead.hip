@@ -1,8 +1,8 @@
 // lmhead.hip -- greedy decoding's token hand-off on the GPU.
 //
-// [Lily-M5] "Decode: minimize bytes per token": between decode steps the token
-// never returns to the CPU; the GPU takes the argmax of the output logits and
-// writes the token ID straight into the next step's input slot.  Here that is
+// [Lily-M5] "Decode: minimize bytes per token": the greedy token stays on the
+// device between decode steps -- the largest output logit picks it and it goes
+// straight into the following step's input.  Here that is
 // two kernels on the caller's stream:
 //   1. lm_head_kernel: logits = head . x, a dequantising GEMV over the V x d Q4
 //      output head (the experts' format, used as bf16 weights, fp32 sums),

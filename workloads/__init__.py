@@ -7,8 +7,8 @@ it returns, so it is the one piece of code the two sides share.
 
 The layer shape is that of Qwen3.6-35B-A3B's MoE FFN as the page "Perplexity's
 Lily beats MLX-LM on MacBook M5 because it only runs one model" describes it
-(section "Why Qwen3.6-35B-A3B is a weird workload": a router scores 256
-experts, picks 8 and adds one shared expert), with the group-64 affine 4-bit
+(section "Why Qwen3.6-35B-A3B is a weird workload": 8 of 256 routed experts
+per token plus 1 always-on shared expert), with the group-64 affine 4-bit
 weight format of its section "Prefill: keep routing on the GPU, dequantize in
 flight" (a bf16 scale and a bf16 bias per group of 64 weights).
 
@@ -155,8 +155,8 @@ def random_x(rng: np.random.Generator, T: int, d: int) -> np.ndarray:
 
 
 # ---- the greedy token hand-off (section "Decode: minimize bytes per token":
-# the GPU takes the argmax of the output logits and writes the token ID into
-# the next step's input slot).  The pages give neither the vocabulary size nor
+# the chosen token stays on the device, from the largest output logit into the
+# following step's input).  The pages give neither the vocabulary size nor
 # the format of the output head and the embedding table; both are taken as
 # V x d matrices in the experts' Q4 format, with the experts' value
 # distributions.  Draw order from PCG64(seed): x, head, embedding table.
