@@ -208,6 +208,23 @@ int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t
                       const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+   tight serving loops, harnesses that forbid hipMalloc): moe_decode_tokens with
+   its workspace taken from a static device array inside the library, of
+   MOE_STATIC_SCRATCH_BYTES bytes, one per GPU for the life of the process.
+   The call allocates nothing (no hipMalloc, no library routine that does);
+   the caller still passes x, y and the optional routing outputs.  Arguments,
+   results and errors are moe_decode_tokens's, plus MOE_EUNSUPPORTED when the
+   layer's decode scratch (what moe_workspace_bytes(L, 1) gives, less the
+   prefill part) exceeds MOE_STATIC_SCRATCH_BYTES.  Every call on a GPU
+   shares that GPU's array: calls that overlap in time on one GPU (different
+   streams, or different host threads without ordering) race and give
+   undefined results.  On the first call on each device the library looks up
+   that device's array (hipGetSymbolAddress, with the device current). */
+#define MOE_STATIC_SCRATCH_BYTES (1u << 20)
+int moe_decode_tokens_static(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                             const moe_routing* r, uint16_t* y, void* stream);
+
 /* Greedy decoding's token hand-off ([Lily-M5] "Decode: minimize bytes per
    token": the chosen token stays on the device between decode steps -- the
    largest output logit selects it and it feeds the following step's input

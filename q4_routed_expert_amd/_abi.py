@@ -14,12 +14,13 @@ MOE_ROUTE_BLOCK = 256
 MOE_DECODE_ROUTER_ROWS = 128
 MOE_MAX_DECODE_TOKENS = 8
 MOE_MAX_VOCAB = 1 << 20
+MOE_STATIC_SCRATCH_BYTES = 1 << 20
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_D, MOE_MAX_INTER = 256, 8, 32768, 8192, 2048
 
 # every function include/q4moe.h declares
 EXPORTS = ("moe_block_map_capacity", "moe_workspace_bytes", "moe_route", "moe_prefill", "moe_trace_events",
            "moe_decode", "moe_decode_tokens", "moe_dequant", "moe_strerror", "moe_last_error",
-           "moe_lm_workspace_bytes", "moe_lm_argmax")
+           "moe_lm_workspace_bytes", "moe_lm_argmax", "moe_decode_tokens_static")
 
 
 class Q4Mat(C.Structure):
@@ -70,12 +71,13 @@ def lib():
         L.moe_prefill.argtypes = [vp, vp, i32, vp, vp, C.c_size_t, vp, vp]
         L.moe_decode.argtypes = [vp, vp, C.c_uint32, vp, vp, C.c_size_t, vp, vp]
         L.moe_decode_tokens.argtypes = [vp, vp, i32, C.c_uint32, vp, vp, C.c_size_t, vp, vp]
+        L.moe_decode_tokens_static.argtypes = [vp, vp, i32, C.c_uint32, vp, vp, vp]
         L.moe_dequant.argtypes = [vp, i32, i32, vp, vp]
         L.moe_lm_workspace_bytes.argtypes = [vp]
         L.moe_lm_workspace_bytes.restype = C.c_size_t
         L.moe_lm_argmax.argtypes = [vp, vp, C.c_uint32, vp, vp, vp, vp, C.c_size_t, vp]
         for f in ("moe_route", "moe_prefill", "moe_decode", "moe_decode_tokens", "moe_dequant",
-                  "moe_lm_argmax"):
+                  "moe_lm_argmax", "moe_decode_tokens_static"):
             getattr(L, f).restype = C.c_int
         L.moe_trace_events.argtypes = [vp, i32]
         L.moe_trace_events.restype = None

@@ -4,6 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 #include "lmhead.h"
 
@@ -251,12 +254,15 @@ int moe_decode(const moe_layer* L, const uint16_t* x, uint32_t flags, const moe_
     return moe_decode_tokens(L, x, 1, flags, r, ws, ws_bytes, y, stream);
 }
 
-int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
-                      const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the decode entry points (everything but the workspace).
+int check_decode(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                 const moe_routing* r, const uint16_t* y) {
     int rc;
-    if ((rc = check_layer(L)) || (rc = check_ptr(y, "y")) || (rc = check_ptr(ws, "workspace")))
-        return rc;
+    if ((rc = check_layer(L)) || (rc = check_ptr(y, "y"))) return rc;
     if (T < 1 || T > MOE_MAX_DECODE_TOKENS)
         return fail(MOE_EUNSUPPORTED, "decode takes 1..%d tokens, not T=%d", MOE_MAX_DECODE_TOKENS,
                     T);
@@ -271,11 +277,13 @@ int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t
             (rc = check_ptr(r->topk_w, "routing.topk_w", true)))
             return rc;
     }
-    const size_t need = moe_workspace_bytes(L, 1);
-    if (ws_bytes < need)
-        return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return MOE_OK;
+}
+
+// The decode launches with the decode region of the workspace at `base`.
+int decode_launch(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                  const moe_routing* r, unsigned char* base, uint16_t* y, void* stream) {
     const DecodeWs dw = decode_ws(L);
-    unsigned char* base = (unsigned char*)ws;
     q4moe::DecodeArgs a;
     a.x = x;
     a.T = T;
@@ -291,7 +299,7 @@ int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t
     a.sh_gate = q4(L->sh_gate);
     a.sh_up = q4(L->sh_up);
     a.sh_down = q4(L->sh_down);
-    a.logits_in = logits_in;
+    a.logits_in = (flags & MOE_LOGITS_IN) != 0;
     a.logits = (r && r->logits) ? r->logits : (float*)(base + dw.logits);
     a.out_idx = r ? r->topk_idx : nullptr;
     a.out_w = r ? r->topk_w : nullptr;
@@ -302,6 +310,79 @@ int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t
     a.y = y;
     trace_begin((hipStream_t)stream);
     return hip_status(q4moe::launch_decode(a, (hipStream_t)stream), "decode");
+}
+
+// Scratch of moe_decode_tokens_static: one copy per GPU, for the life of the
+// process.  Host code never uses this name as an address (in host code it is
+// a stand-in, not device memory); it uses the per-device address that
+// hipGetSymbolAddress returns.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned char*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's scratch address, looked up once per device with that
+// device current.  NULL (and the reason in the error text) on failure.
+unsigned char* static_scratch(int* rc) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = fail(MOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *rc = fail(MOE_EUNSUPPORTED, "device %d is beyond the %d the library tracks", dev,
+                   kMaxDevices);
+        return nullptr;
+    }
+    unsigned char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !addr) {
+            *rc = fail(MOE_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                       hipGetErrorString(e));
+            return nullptr;
+        }
+        p = (unsigned char*)addr;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_decode_tokens_static(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                             const moe_routing* r, uint16_t* y, void* stream) {
+    int rc;
+    if ((rc = check_decode(L, x, T, flags, r, y))) return rc;
+    const size_t need = decode_ws(L).total;
+    if (need > kStaticScratchBytes)
+        return fail(MOE_EUNSUPPORTED,
+                    "this layer's decode scratch (%zu bytes) exceeds the library's static %zu",
+                    need, kStaticScratchBytes);
+    unsigned char* base = static_scratch(&rc);
+    if (!base) return rc;
+    return decode_launch(L, x, T, flags, r, base, y, stream);
+}
+
+int moe_decode_tokens(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
+                      const moe_routing* r, void* ws, size_t ws_bytes, uint16_t* y,
+                      void* stream) {
+    int rc;
+    if ((rc = check_decode(L, x, T, flags, r, y)) || (rc = check_ptr(ws, "workspace")))
+        return rc;
+    const size_t need = moe_workspace_bytes(L, 1);
+    if (ws_bytes < need)
+        return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return decode_launch(L, x, T, flags, r, (unsigned char*)ws, y, stream);
 }
 
 int moe_dequant(const moe_q4mat* m, int32_t n_rows, int32_t K, uint16_t* w_out, void* stream) {

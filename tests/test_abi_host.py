@@ -176,6 +176,20 @@ def test_router_loads_stay_inside_their_k_slice():
                         assert kk == k + 8 * half
 
 
+def test_static_scratch_decode_validates_before_launch():
+    lib = _abi.lib()
+    L = _layer()
+    assert lib.moe_decode_tokens_static(C.addressof(L), FAKE, 9, 0, None, FAKE,
+                                        None) == _abi.MOE_EUNSUPPORTED
+    assert lib.moe_decode_tokens_static(C.addressof(L), FAKE, 1, 2, None, FAKE,
+                                        None) == _abi.MOE_EINVAL
+    assert lib.moe_decode_tokens_static(C.addressof(L), FAKE, 1, 0, None, None,
+                                        None) == _abi.MOE_EINVAL
+    bad = _layer(d=100)
+    assert lib.moe_decode_tokens_static(C.addressof(bad), FAKE, 1, 0, None, FAKE,
+                                        None) == _abi.MOE_EUNSUPPORTED
+
+
 def test_block_map_capacity_bounds_the_tile_count():
     lib = _abi.lib()
     # sum over experts of ceil(c/rows) <= floor(T*k/rows) + min(E, T*k)
