@@ -241,7 +241,6 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
     a.h_sh = (uint16_t*)(base + pw.h_sh);
     a.part = (uint16_t*)(base + pw.part);
     a.pexp = (int8_t*)(base + pw.pexp);
-    a.sh_rows = 0;  // chosen by the launcher
     a.dn_pre = (int32_t*)(base + pw.dn_pre);
     a.dn_exp = (int32_t*)(base + pw.dn_exp);
     a.y = y;

@@ -41,7 +41,6 @@ struct PrefillArgs {
     uint16_t* part;      // fp16 [T*k][d], routed expert outputs scaled by 2^-pexp, rows in
                          // assignment order
     int8_t* pexp;        // [T][d/32][8] staging exponent per (token, 32 columns, slot)
-    int sh_rows;         // tokens per item of the shared expert's down projection
     int32_t* dn_pre;     // [items + 1] the down kernel's item cost prefix (NULL: not used)
     int32_t* dn_exp;     // [items] the down kernel's item experts (-1: shared)
     uint16_t* y;         // bf16 [T][d]

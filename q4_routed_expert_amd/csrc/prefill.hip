@@ -53,6 +53,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 4;             // weight chunks held in registers
 constexpr int kALoads = kMT * kSlots / kThreads;
 constexpr int kPartCols = 32;          // columns per staging exponent
+constexpr int kDnCols = 256;           // output columns of a down work unit: 8 waves x 32
 static_assert(kMT * kSlots % kThreads == 0, "A tile split");
 
 template <int N>
@@ -147,66 +148,6 @@ __device__ __forceinline__ void routed_store(const PrefillArgs& a, int dst, int 
     }
 }
 
-// The shared expert's outputs of token tok (a lane pair's row) and the combine:
-// y[tok][c] = bf16( sum_{s<k} w[tok,s] * part[tok*k+s][c] (slot order) +
-// shared[c] ) for the pair's 32 columns from wc.  All k partial loads of a lane
-// are issued before any arithmetic.
-__device__ __forceinline__ void combine_store(const PrefillArgs& a, int tok, int wc, int half,
-                                              const f32x16& acc) {
-    const int k = a.k;
-    float sh[2][8];  // this lane's two runs of 8 columns (16m + 8h .. +7)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        float own_lo[4], own_hi[4], send[4], recv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            own_lo[i] = acc[4 * (2 * m) + i];      // group 2m (kept by h = 0)
-            own_hi[i] = acc[4 * (2 * m + 1) + i];  // group 2m + 1 (kept by h = 1)
-            send[i] = half ? own_lo[i] : own_hi[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) recv[i] = __shfl_xor(send[i], 32, 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sh[m][i] = half ? recv[i] : own_lo[i];
-            sh[m][4 + i] = half ? own_hi[i] : recv[i];
-        }
-    }
-    const uint16_t* prow = a.part + (size_t)tok * k * a.d + wc + 8 * half;
-    u32x4 p[2][kMaxTopK];
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-            p[m][s] = *(const u32x4*)(prow + (size_t)(s < k ? s : 0) * a.d + 16 * m);
-    const uint2 ex = *(const uint2*)(a.pexp + part_exp_index(a, tok * k, wc));
-    float w[kMaxTopK];
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) w[s] = a.topk_w[(size_t)tok * k + (s < k ? s : 0)];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s) {
-            if (s < k) {
-                const int e = (int)(int8_t)(((s < 4 ? ex.x : ex.y) >> (8 * (s & 3))) & 0xFFu);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float lo = __builtin_amdgcn_ldexpf(f16_to_f32(p[m][s][i] & 0xFFFFu), e);
-                    const float hi = __builtin_amdgcn_ldexpf(f16_to_f32(p[m][s][i] >> 16), e);
-                    acc8[2 * i] += w[s] * lo;
-                    acc8[2 * i + 1] += w[s] * hi;
-                }
-            }
-        }
-        u32x4 out;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out[i] = pack_bf16x2(acc8[2 * i] + sh[m][2 * i], acc8[2 * i + 1] + sh[m][2 * i + 1]);
-        *(u32x4*)(a.y + (size_t)tok * a.d + wc + 16 * m + 8 * half) = out;
-    }
-}
-
 // One lane's share of one weight chunk: k in [kc + 32h, +32) (group kc/64)
 // and [kc + 64 + 32h, +32) (group kc/64 + 1), h = lane / 32.  Scales and
 // biases stay raw bf16 bits until use: converting them right after the load
@@ -235,72 +176,32 @@ __device__ __forceinline__ void load_bchunk(const Q4& W, size_t wrow, int K, int
     }
 }
 
-// Any inter (a multiple of 64): the activation tile streams through LDS one
-// K-chunk at a time, double buffered, one barrier per chunk; each wave owns
-// 32 output columns of a 256-column block.
-//   kShared = false: the routed work map (item = routed 128-row work item);
-//                    outputs go to `part` (routed_store).
-//   kShared = true:  the shared expert over blocks of a.sh_rows tokens (item =
-//                    token block, at most 128 rows); the epilogue combines
-//                    (combine_store) and writes y.
-template <bool kShared>
-__global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArgs a,
-                                                                const int n_items, const int n_cb,
-                                                                const int n_wg) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
-    __shared__ int s_src[kMT];  // activation row per tile row (-1: none)
-    __shared__ int s_dst[kMT];  // output row per tile row (assignment, or token)
-
-    // XCD-aware order: consecutive logical indices (the column blocks of one
-    // item, which share the activation rows) stay on one XCD's L2.
-    const int b = blockIdx.x;
-    const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
-    const int item = L / n_cb, cb = L - item * n_cb;
-    if (item >= n_items) return;
-    DownItem it;
-    if (kShared) {
-        it.e = 0;
-        it.row0 = item * a.sh_rows;
-        it.M = min(a.sh_rows, a.T - it.row0);
-    } else if (!routed_item(a, item, it)) {
-        return;
-    }
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-    const int K = a.I, Nw = a.d;
-    const uint16_t* A = kShared ? a.h_sh : a.h;
-    const Q4 W = kShared ? a.sh_down : a.down;
-    if (tid < kMT) {
-        int src = -1, dst = -1;
-        if (tid < it.M) {
-            src = it.row0 + tid;
-            dst = kShared ? src : a.perm[src];
-        }
-        s_src[tid] = src;
-        s_dst[tid] = dst;
-    }
-    __syncthreads();
-
-    const int n_ms = (it.M + 31) >> 5;  // active 32-row subtiles
-    const int wcol0 = cb * 256 + 32 * wave;
-    const bool wave_on = wcol0 < Nw;
-    const int col = wcol0 + (lane & 31);  // this lane's weight row
+// One work item's down GEMM with the activation tile streamed through LDS one
+// K-chunk at a time (any inter, a multiple of 64), double buffered, one
+// barrier per chunk; each wave owns 32 output columns (weight rows wrow..) and
+// accumulates acc[ms] for the NMS active 32-row subtiles.  The tile has kRowsT
+// rows; src_row[p] is the activation row of tile row (tid + kThreads p) / 16
+// (-1: none, zeros).  Contains barriers: every thread of the work group calls
+// it with the same NMS.
+template <int kRowsT, int NMS>
+__device__ __forceinline__ void chunk_gemm(const uint16_t* A, const int (&src_row)[kRowsT * kSlots / kThreads],
+                                           int K, const Q4& W, size_t wrow, bool wave_on,
+                                           unsigned char* lds, f32x16 (&acc)[4]) {
+    constexpr int kAL = kRowsT * kSlots / kThreads;  // 16-byte activation loads per thread per chunk
+    constexpr int kBuf = kRowsT * kRowBytes;
+    static_assert(kRowsT * kSlots % kThreads == 0 && 32 * NMS <= kRowsT, "tile split");
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int n_chunks = (K + kKC - 1) / kKC;
-    const size_t wrow = (size_t)it.e * Nw + (wave_on ? col : 0);
-
-    u32x4 ast[kStages][kALoads];  // activation chunks in flight (same depth as the weights)
+    u32x4 ast[kStages][kAL];  // activation chunks in flight (same depth as the weights)
     BChunk bst[kStages];
-    int src_row[kALoads];
-#pragma unroll
-    for (int p = 0; p < kALoads; ++p) src_row[p] = s_src[(tid + kThreads * p) >> 4];
 
     // Loads are issued unconditionally from always-valid (clamped) addresses
     // and invalid data is zeroed where it is used: a load under a branch makes
     // the compiler's wait-count analysis fall back to waiting for every
     // outstanding load, which would serialise the pipeline.
-    auto load_a = [&](int c, u32x4 (&areg)[kALoads]) {
+    auto load_a = [&](int c, u32x4 (&areg)[kAL]) {
 #pragma unroll
-        for (int p = 0; p < kALoads; ++p) {
+        for (int p = 0; p < kAL; ++p) {
             const int slot = (tid + kThreads * p) & 15;
             const int kcol = c * kKC + 8 * slot;
             const int src = src_row[p];
@@ -308,13 +209,13 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
             areg[p] = *(const u32x4*)(A + off);
         }
     };
-    auto store_a = [&](int c, int buf, const u32x4 (&areg)[kALoads]) {
+    auto store_a = [&](int c, int buf, const u32x4 (&areg)[kAL]) {
 #pragma unroll
-        for (int p = 0; p < kALoads; ++p) {
+        for (int p = 0; p < kAL; ++p) {
             const int i = tid + kThreads * p, row = i >> 4, slot = i & 15;
             const bool ok = src_row[p] >= 0 && c * kKC + 8 * slot < K;
             const u32x4 z = {0u, 0u, 0u, 0u};
-            *(u32x4*)(lds + buf * kTileBytes + lds_off(row, slot)) = ok ? areg[p] : z;
+            *(u32x4*)(lds + buf * kBuf + lds_off(row, slot)) = ok ? areg[p] : z;
         }
     };
     const bool pair_sb = (K / kGroup) % 2 == 0;
@@ -324,16 +225,10 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
         load_bchunk(W, wrow, K, kc0, kc1, half, pair_sb, st);
     };
 
-    f32x16 acc[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
-
-    // One chunk on the matrix cores for NMS active 32-row subtiles (a compile-
-    // time count, so the inner loop has no branches).  The activation
-    // fragments of step j+1 are read from LDS while step j's MFMAs run.
-    auto compute = [&](auto nms_tag, int c, int buf, const BChunk& st) {
-        constexpr int NMS = decltype(nms_tag)::value;
-        const unsigned char* tile = lds + buf * kTileBytes;
+    // One chunk on the matrix cores.  The activation fragments of step j+1 are
+    // read from LDS while step j's MFMAs run.
+    auto compute = [&](int c, int buf, const BChunk& st) {
+        const unsigned char* tile = lds + buf * kBuf;
         // chunks (or second halves) past K contribute zero weights
         const bool ok0 = c * kKC < K, ok1 = c * kKC + kGroup < K;
         const float s0 = ok0 ? dq_scale(st.sp & 0xFFFFu) : 0.0f, b0 = ok0 ? bf16_to_f32(st.bp & 0xFFFFu) : 0.0f;
@@ -368,30 +263,70 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
     // loop runs a multiple of kStages chunks; chunks past K load clamped
     // addresses (recently read lines) and contribute zeros.
     const int n_loop = (n_chunks + kStages - 1) / kStages * kStages;
-    auto main_loop = [&](auto nms_tag) {
 #pragma unroll
-        for (int u = 0; u < kStages - 1; ++u) {
-            load_a(u, ast[u]);
-            load_b(u, bst[u]);
-        }
-        for (int c0 = 0; c0 < n_loop; c0 += kStages) {
+    for (int u = 0; u < kStages - 1; ++u) {
+        load_a(u, ast[u]);
+        load_b(u, bst[u]);
+    }
+    for (int c0 = 0; c0 < n_loop; c0 += kStages) {
 #pragma unroll
-            for (int u = 0; u < kStages; ++u) {
-                const int c = c0 + u;
-                store_a(c, u & 1, ast[u]);
-                __syncthreads();
-                const int nx = (u + kStages - 1) % kStages;
-                load_a(c + kStages - 1, ast[nx]);
-                load_b(c + kStages - 1, bst[nx]);
-                if (wave_on) compute(nms_tag, c, u & 1, bst[u]);
-            }
+        for (int u = 0; u < kStages; ++u) {
+            const int c = c0 + u;
+            store_a(c, u & 1, ast[u]);
+            __syncthreads();
+            const int nx = (u + kStages - 1) % kStages;
+            load_a(c + kStages - 1, ast[nx]);
+            load_b(c + kStages - 1, bst[nx]);
+            if (wave_on) compute(c, u & 1, bst[u]);
         }
-    };
+    }
+}
+
+// Routed rows, any inter: one 128-row work item of the routed work map x one
+// 256-column block per work group; outputs go to `part` (routed_store).
+__global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArgs a,
+                                                                const int n_items, const int n_cb,
+                                                                const int n_wg) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileBytes];
+    __shared__ int s_src[kMT];  // activation row per tile row (-1: none)
+    __shared__ int s_dst[kMT];  // output row (assignment) per tile row
+
+    // XCD-aware order: consecutive logical indices (the column blocks of one
+    // item, which share the activation rows) stay on one XCD's L2.
+    const int b = blockIdx.x;
+    const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
+    const int item = L / n_cb, cb = L - item * n_cb;
+    if (item >= n_items) return;
+    DownItem it;
+    if (!routed_item(a, item, it)) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    if (tid < kMT) {
+        int src = -1, dst = -1;
+        if (tid < it.M) {
+            src = it.row0 + tid;
+            dst = a.perm[src];
+        }
+        s_src[tid] = src;
+        s_dst[tid] = dst;
+    }
+    __syncthreads();
+
+    const int n_ms = (it.M + 31) >> 5;  // active 32-row subtiles
+    const int wcol0 = cb * kDnCols + 32 * wave;
+    const bool wave_on = wcol0 < a.d;
+    const size_t wrow = (size_t)it.e * a.d + (wave_on ? wcol0 + (lane & 31) : 0);
+    int src_row[kALoads];
+#pragma unroll
+    for (int p = 0; p < kALoads; ++p) src_row[p] = s_src[(tid + kThreads * p) >> 4];
+    f32x16 acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
     switch (n_ms) {
-        case 1: main_loop(Int<1>{}); break;
-        case 2: main_loop(Int<2>{}); break;
-        case 3: main_loop(Int<3>{}); break;
-        default: main_loop(Int<4>{}); break;
+        case 1: chunk_gemm<kMT, 1>(a.h, src_row, a.I, a.down, wrow, wave_on, lds, acc); break;
+        case 2: chunk_gemm<kMT, 2>(a.h, src_row, a.I, a.down, wrow, wave_on, lds, acc); break;
+        case 3: chunk_gemm<kMT, 3>(a.h, src_row, a.I, a.down, wrow, wave_on, lds, acc); break;
+        default: chunk_gemm<kMT, 4>(a.h, src_row, a.I, a.down, wrow, wave_on, lds, acc); break;
     }
 
     if (!wave_on) return;
@@ -399,10 +334,140 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
     for (int ms = 0; ms < 4; ++ms) {
         const int row = 32 * ms + (lane & 31);
         if (ms >= n_ms || row >= it.M) continue;
-        if (kShared)
-            combine_store(a, s_dst[row], wcol0, half, acc[ms]);
+        routed_store(a, s_dst[row], wcol0, half, acc[ms]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The shared expert's down projection with the combine.  Work item = a block of
+// kRows (32 or 64) tokens x 256 output columns.  Three phases:
+//   1. the k staged partial rows of every token of the block are read with
+//      contiguous 16-byte loads (32 threads cover one token's 256 columns, every
+//      load issued before any is used), unscaled, weighted by the scores and
+//      summed in slot order into an fp32 tile in LDS;
+//   2. the shared expert's down GEMM of the block (chunk_gemm);
+//   3. y = bf16(routed sum + shared output), staged through LDS so that the
+//      global stores are contiguous 16-byte pieces.
+// ---------------------------------------------------------------------------
+constexpr int kShMaxRows = 64;
+
+// 16-byte granule g of row r of the routed-sum tile (1 KB rows), XOR-swizzled
+// by row so that a subtile's 32 rows read at one column spread over the banks.
+__device__ __forceinline__ int rsum_off(int r, int g) { return r * 1024 + ((g ^ (r & 63)) << 4); }
+// 16-byte granule g of row r of the bf16 output tile (512-byte rows).
+__device__ __forceinline__ int ytile_off(int r, int g) { return r * 512 + ((g ^ (r & 31)) << 4); }
+
+template <int kRows>
+__global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const PrefillArgs a,
+                                                                       const int n_items,
+                                                                       const int n_cb,
+                                                                       const int n_wg) {
+    static_assert(kRows == 32 || kRows == 64, "shared rows");
+    constexpr int kP = kRows * 32 / kThreads;  // tokens per thread in the routed-sum phase
+    constexpr int kAL = kRows * kSlots / kThreads;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kShMaxRows * kRowBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_rsum[kShMaxRows * 1024];
+    __shared__ float s_w[kShMaxRows * kMaxTopK];
+
+    const int b = blockIdx.x;
+    const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
+    const int item = L / n_cb, cb = L - item * n_cb;
+    if (item >= n_items) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int T = a.T, d = a.d, k = a.k;
+    const int row0 = item * kRows, M = min(kRows, T - row0);
+    const int c0 = cb * kDnCols;
+
+    // ---- 1. routed sums: thread (token row tr0 + 16 p, columns c0 + 8 c8 ..) ----
+    const int c8 = tid & 31, tr0 = tid >> 5;
+    const int col = c0 + 8 * c8;
+    const bool col_ok = col < d;  // d is a multiple of 64: 8-column pieces are whole
+    const int colc = col_ok ? col : c0;
+    u32x4 pv[kP][kMaxTopK];
+    uint2 ev[kP];
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        const int tr = tr0 + 16 * p;
+        const size_t tok = (size_t)row0 + (tr < M ? tr : 0);  // clamped, always valid
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+            pv[p][s] = *(const u32x4*)(a.part + (tok * k + (s < k ? s : 0)) * d + colc);
+        ev[p] = *(const uint2*)(a.pexp + part_exp_index(a, (int)tok * k, colc));
+    }
+    for (int i = tid; i < kRows * k; i += kThreads)
+        s_w[i] = row0 + i / k < T ? a.topk_w[(size_t)row0 * k + i] : 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        const int tr = tr0 + 16 * p;
+        if (tr < M && col_ok) {
+            float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < kMaxTopK; ++s) {
+                if (s < k) {
+                    const float w = s_w[tr * k + s];
+                    const int e = (int)(int8_t)(((s < 4 ? ev[p].x : ev[p].y) >> (8 * (s & 3))) & 0xFFu);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc8[2 * i] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] & 0xFFFFu), e);
+                        acc8[2 * i + 1] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] >> 16), e);
+                    }
+                }
+            }
+            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8)) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
+            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8 + 1)) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
+        }
+    }
+
+    // ---- 2. the shared expert's down GEMM of the block ----
+    const int wcol0 = c0 + 32 * wave;
+    const bool wave_on = wcol0 < d;
+    const size_t wrow = wave_on ? (size_t)(wcol0 + (lane & 31)) : 0;
+    int src_row[kAL];
+#pragma unroll
+    for (int p = 0; p < kAL; ++p) {
+        const int r = (tid + kThreads * p) >> 4;
+        src_row[p] = r < M ? row0 + r : -1;
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+    const int n_ms = (M + 31) >> 5;
+    if constexpr (kRows == 64) {
+        if (n_ms == 2)
+            chunk_gemm<kRows, 2>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
         else
-            routed_store(a, s_dst[row], wcol0, half, acc[ms]);
+            chunk_gemm<kRows, 1>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
+    } else {
+        chunk_gemm<kRows, 1>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
+    }
+    __syncthreads();  // every wave is done with the activation tiles (the y tile reuses them)
+
+    // ---- 3. y = bf16(routed sum + shared output) ----
+    // lane: tile row 32 ms + lane % 32, columns 8 g + 4 h .. +3 of its wave's 32
+    if (wave_on) {
+#pragma unroll
+        for (int ms = 0; ms < 2; ++ms) {
+            const int r = 32 * ms + (lane & 31);
+            if (ms < n_ms && r < M) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int cl = 32 * wave + 8 * g + 4 * half;  // column within the block
+                    const f32x4 rs = *(const f32x4*)(s_rsum + rsum_off(r, cl >> 2));
+                    uint2 v;
+                    v.x = pack_bf16x2(rs[0] + acc[ms][4 * g], rs[1] + acc[ms][4 * g + 1]);
+                    v.y = pack_bf16x2(rs[2] + acc[ms][4 * g + 2], rs[3] + acc[ms][4 * g + 3]);
+                    *(uint2*)(lds + ytile_off(r, cl >> 3) + 8 * half) = v;
+                }
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        const int tr = tr0 + 16 * p;
+        if (tr < M && col_ok)
+            *(u32x4*)(a.y + (size_t)(row0 + tr) * d + col) = *(const u32x4*)(lds + ytile_off(tr, c8));
     }
 }
 
@@ -491,7 +556,6 @@ __device__ __forceinline__ int run_start(int g, int G, int n_items, int n_cb, co
 // last chunk is done.
 // ---------------------------------------------------------------------------
 constexpr int kDnMaxI = 512;
-constexpr int kDnCols = 256;  // output columns per unit: 8 waves x 32
 
 // The down kernel's schedule: the routed items' cost prefix over (n_cb
 // 256-column units per item) and their experts, written to the workspace by
@@ -1399,36 +1463,36 @@ static hipError_t launch_down_routed(const PrefillArgs& a, hipStream_t s) {
             hipLaunchKernelGGL(down_resident_kernel<false>, dim3(grid), dim3(kThreads), 0, s, a, n_cb);
     } else {
         const int n_wg = ((a.tile_bound * n_cb) + 7) & ~7;
-        hipLaunchKernelGGL(down_chunked_kernel<false>, dim3(n_wg), dim3(kThreads), 0, s, a,
-                           a.tile_bound, n_cb, n_wg);
+        hipLaunchKernelGGL(down_chunked_kernel, dim3(n_wg), dim3(kThreads), 0, s, a, a.tile_bound,
+                           n_cb, n_wg);
     }
     trace_point(s);
     return hipGetLastError();
 }
 
-// Rows per shared-expert down item: the tallest of 128, 64, 32 that still
-// gives every CU a work group (at least twice over for 128), so the combine's
-// reads of the staged rows are spread over the whole chip.
+// Rows per shared-expert down item: 64, or 32 where 64-token items would leave
+// CUs without a work group (the combine's reads of the staged rows are then
+// spread over the whole chip).
 static int shared_down_rows(int T, int n_cb) {
-    const int cus = device_cus();
-    if ((T + 127) / 128 * n_cb >= 2 * cus) return 128;
-    if ((T + 63) / 64 * n_cb >= cus) return 64;
-    return 32;
+    return (T + 63) / 64 * n_cb >= device_cus() ? 64 : 32;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a_in, hipStream_t s) {
-    hipError_t err = launch_gate_up(a_in, s);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    hipError_t err = launch_gate_up(a, s);
     if (err != hipSuccess) return err;
-    err = launch_down_routed(a_in, s);
+    err = launch_down_routed(a, s);
     if (err != hipSuccess) return err;
-    // the shared expert's down projection with the combine in its epilogue
-    PrefillArgs a = a_in;
-    const int n_cb = (a.d + 255) / 256;
-    a.sh_rows = shared_down_rows(a.T, n_cb);
-    const int n_items = (a.T + a.sh_rows - 1) / a.sh_rows;
+    // the shared expert's down projection with the combine
+    const int n_cb = (a.d + kDnCols - 1) / kDnCols;
+    const int rows = shared_down_rows(a.T, n_cb);
+    const int n_items = (a.T + rows - 1) / rows;
     const int n_wg = ((n_items * n_cb) + 7) & ~7;
-    hipLaunchKernelGGL(down_chunked_kernel<true>, dim3(n_wg), dim3(kThreads), 0, s, a, n_items,
-                       n_cb, n_wg);
+    if (rows == 64)
+        hipLaunchKernelGGL(shared_down_combine_kernel<64>, dim3(n_wg), dim3(kThreads), 0, s, a,
+                           n_items, n_cb, n_wg);
+    else
+        hipLaunchKernelGGL(shared_down_combine_kernel<32>, dim3(n_wg), dim3(kThreads), 0, s, a,
+                           n_items, n_cb, n_wg);
     trace_point(s);
     return hipGetLastError();
 }
