@@ -7,23 +7,22 @@
 // projections fused with the gate activation, the output projection fused
 // with the routing scores and the shared expert, intermediates in registers.
 //
-// Three launches on one stream (every launch boundary costs several
-// microseconds at batch 1, so the work is packed into as few as the data
-// dependencies allow), each spread over thousands of waves so that the
-// weight loads of many waves are in flight at once:
-//   1. router partial sums (ceil(d/128) work groups, each sums 128 rows of
-//      x . W_r for every expert, a whole row per load instruction; skipped
-//      when the logits are given) and, in
-//      the same launch, the shared expert's gate/up rows, which need no
-//      routing;
+// Three launches on one stream (a launch boundary costs about as much as a
+// grid-wide wait inside one kernel on this chip, so the two cross-work-group
+// dependencies -- the top-k needs every logit, the down projection every h
+// value -- are kernel boundaries), each spread over hundreds of work groups so
+// that the weight loads of many waves are in flight at once:
+//   1. router partial sums over blocks of 128 rows x 64 experts of W_r
+//      (skipped when the logits are given) and, in the same launch, the shared
+//      expert's gate/up rows, which need no routing;
 //   2. every work group adds the partial sums in a fixed order (+ bias) and
 //      runs the top-k itself -- the same arithmetic in every work group, so
 //      every one finds the same experts -- then computes gate/up rows of its
 //      routed slot: one wave per (slot, intermediate row j), the gate and up
 //      rows streamed once with 16-byte loads per lane, h = bf16(SiLU(g) * u);
-//   3. down: one wave per output n (several for larger T): each lane takes
-//      one code word of each of the k + 1 experts' rows, and the wave combines
-//      y = bf16( sum_s w_s * P_s (slot order) + P_shared ).
+//   3. down: 16 lanes per (output row, expert) task, 16-byte pieces per lane;
+//      the selected experts, h and every weight piece are loaded before any
+//      arithmetic, and y = bf16( sum_s w_s * P_s (slot order) + P_shared ).
 // Every weight enters as the bf16 value bf16(q * s + b), the same operand the
 // grouped GEMM feeds its matrix cores, so prefill and decode compute one
 // function of the layer.
@@ -32,15 +31,12 @@
 namespace q4moe {
 
 constexpr int kRouterRows = 128;  // rows of W_r per router work group (DecodeWs sizes partial by it)
-constexpr int kRouterWaves = 16;
-constexpr int kRouterWaveRows = kRouterRows / kRouterWaves;
 constexpr int kDecRows = 16;  // gate/up rows per 1024-thread work group, one wave each
-constexpr int kDownWaves = 8;  // down outputs per work group, one wave each
 constexpr int kSharedTokens = 2;  // tokens per shared-expert gate/up work group
+constexpr int kSharedRowsPerGroup = 4;  // shared gate/up rows per work group (one per wave)
 
 static_assert(kRouterRows == MOE_DECODE_ROUTER_ROWS, "router partial rows");
 static_assert(MOE_MAX_DECODE_TOKENS == 8, "token buckets 1, 2, 4, 8");
-static_assert(kRouterWaves * 64 == 1024 && 4 * 64 == kMaxExperts, "router work group shape");
 
 // One wave: h[slot][j] = bf16(SiLU(W_gate[e] x)_j * (W_up[e] x)_j) for expert
 // e (or the shared expert); lane covers 32 consecutive k of each 2048-wide
@@ -196,87 +192,111 @@ __device__ __forceinline__ void stage_x(const DecodeArgs& a, uint16_t* s_x, int 
     for (int i = tid; i < n_tok * a.d / 8; i += n_threads) ((u32x4*)s_x)[i] = src[i];
 }
 
-// Work groups [0, n_part): partial[g][t][e] = sum of x[t][r] W_r[r][e] over
-// the 128 rows r of group g, for every token t.  Wave w takes rows
-// 8w .. 8w + 7 of the group, each lane four consecutive experts: one 16-byte
-// load per row and lane, so one load instruction reads a whole 1 KB row of
-// W_r (E = 256), and each W_r row is read once for all tokens; x[t][r] is
-// wave-uniform and comes through the scalar cache.  The sixteen waves' sums
-// are added in wave order through LDS.  Work groups from n_part on: the
-// shared expert's gate/up rows, one per wave, for a group of up to
+// Router work groups: g = rb * n_eb + eb, rb < ceil(d / 128), eb < ceil(E / 64):
+// partial[rb][t][e] = sum of x[t][r] W_r[r][e] over the 128 rows r of row
+// block rb, for the 64 experts e of expert block eb and every token t.  Thread
+// (rr = tid / 16, e4 = tid % 16) takes rows rr, rr + 16, .., rr + 112 and experts
+// 4 e4 .. 4 e4 + 3: one 16-byte load per row, so one load instruction of a
+// wave reads 256 contiguous bytes of each of four rows, and a work group reads
+// 32 KB of W_r.  The block's x slice is staged in LDS first.  Sums: over
+// the thread's rows in order, then over the four row offsets of a wave
+// (shuffles), then over the four waves in order.  Work groups from n_router
+// on: the shared expert's gate/up rows, one per wave, for a group of up to
 // kSharedTokens tokens (more tokens: more work groups).
+constexpr int kRtThreads = 256;
+constexpr int kRtExperts = 64;  // experts per router work group
+static_assert(kRtThreads / 16 * 8 == kRouterRows, "router rows per work group");
+
 template <int NT, bool VEC>
-__global__ __launch_bounds__(1024) void decode_router_shared_kernel(const DecodeArgs a,
-                                                                    int n_part) {
+__global__ __launch_bounds__(kRtThreads) void decode_router_shared_kernel(const DecodeArgs a,
+                                                                          int n_router) {
     constexpr int NS = NT < kSharedTokens ? NT : kSharedTokens;
-    constexpr int kQBytes = kRouterWaves * NT * kMaxExperts * 4, kXBytes = NS * MOE_MAX_D * 2;
-    // the router's partial sums and the shared part's x never share a work group
+    constexpr int kQBytes = 4 * NT * kRtExperts * 4 + NT * kRouterRows * 2;
+    constexpr int kXBytes = NS * MOE_MAX_D * 2;
+    // the router's sums and the shared part's x never share a work group
     __shared__ __attribute__((aligned(16))) unsigned char s_mem[kQBytes > kXBytes ? kQBytes : kXBytes];
-    float* s_q = (float*)s_mem;  // [kRouterWaves][NT][kMaxExperts]
-    uint16_t* s_x = (uint16_t*)s_mem;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int T = a.T;
-    if ((int)blockIdx.x >= n_part) {  // uniform per work group
-        const int n_rows = (a.I + kDecRows - 1) / kDecRows;
-        const int b = (int)blockIdx.x - n_part, rb = b % n_rows, t0 = (b / n_rows) * NS;
+    if ((int)blockIdx.x >= n_router) {  // uniform per work group
+        uint16_t* s_x = (uint16_t*)s_mem;
+        const int n_rows = (a.I + kSharedRowsPerGroup - 1) / kSharedRowsPerGroup;
+        const int b = (int)blockIdx.x - n_router, rb = b % n_rows, t0 = (b / n_rows) * NS;
         const int n_tok = T - t0 < NS ? T - t0 : NS;
-        stage_x(a, s_x, t0, n_tok, tid, 1024);
+        stage_x(a, s_x, t0, n_tok, tid, kRtThreads);
         __syncthreads();
-        const int j = rb * kDecRows + wave;
+        const int j = rb * kSharedRowsPerGroup + wave;
         if (j < a.I) shared_gate_up_rows<NS>(a, s_x, t0, n_tok, j, lane);
         return;
     }
     if (a.logits_in) return;  // uniform
-    const int g = blockIdx.x, E = a.E, d = a.d;
-    const int e0 = 4 * lane;
-    // first row of this wave, made explicitly wave-uniform for the scalar loads of x
-    const int r0 = __builtin_amdgcn_readfirstlane(g * kRouterRows + wave * kRouterWaveRows);
-    u32x4 w[kRouterWaveRows];
+    float* s_q = (float*)s_mem;                                     // [4 waves][NT][64]
+    uint16_t* s_xr = (uint16_t*)(s_mem + 4 * NT * kRtExperts * 4);  // [NT][128]
+    const int E = a.E, d = a.d;
+    const int n_eb = (E + kRtExperts - 1) / kRtExperts;
+    const int rb = (int)blockIdx.x / n_eb, eb = (int)blockIdx.x - rb * n_eb;
+    const int r0 = rb * kRouterRows, rr = tid >> 4, e4 = tid & 15;
+    const int e0 = eb * kRtExperts + 4 * e4;
+    // W_r rows r0 + rr + 16 j: all loads first (clamped, always valid)
+    u32x4 w[8];
 #pragma unroll
-    for (int r = 0; r < kRouterWaveRows; ++r) {
-        const uint32_t rr = (uint32_t)(r0 + r < d ? r0 + r : 0);  // clamped, always valid
+    for (int j = 0; j < 8; ++j) {
+        const int r = r0 + rr + 16 * j;
+        const uint32_t rc = (uint32_t)(r < d ? r : 0);
         if constexpr (VEC) {
             const uint32_t ee = (uint32_t)(e0 < E ? e0 : 0);
-            w[r] = *(const u32x4*)(a.w_router + (rr * (uint32_t)E + ee));
+            w[j] = *(const u32x4*)(a.w_router + (rc * (uint32_t)E + ee));
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t ee = (uint32_t)(e0 + i < E ? e0 + i : 0);
-                w[r][i] = __float_as_uint(a.w_router[rr * (uint32_t)E + ee]);
+                w[j][i] = __float_as_uint(a.w_router[rc * (uint32_t)E + ee]);
             }
         }
     }
-    // x[t][r0 .. r0 + 7]: one uniform 16-byte load per token (r0 is a multiple
-    // of 8 and d of 64)
-    const bool r_ok = r0 < d;
+    // x[t][r0 .. r0 + 127] (d is a multiple of 64, so a row block is whole or
+    // ends at d on a 64-row boundary)
+    for (int i = tid; i < NT * kRouterRows / 8; i += kRtThreads) {
+        const int t = i / (kRouterRows / 8), c = 8 * (i - t * (kRouterRows / 8));
+        const bool ok = t < T && r0 + c < d;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 v = *(const u32x4*)(a.x + ((size_t)(t < T ? t : 0) * d + (ok ? r0 + c : 0)));
+        *(u32x4*)(s_xr + t * kRouterRows + c) = ok ? v : z;
+    }
+    __syncthreads();
     float acc[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int tt = t < T ? t : 0;  // clamped, always valid
-        const u32x4 xq = *(const u32x4*)(a.x + ((size_t)tt * d + (r_ok ? r0 : 0)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < kRouterWaveRows; ++r) {
-            const uint32_t xw = xq[r >> 1];
-            const float xv =
-                r_ok ? __uint_as_float((r & 1) ? (xw & 0xffff0000u) : (xw << 16)) : 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            const float xv = bf16_to_f32(s_xr[t * kRouterRows + rr + 16 * j]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                acc[t][i] = __builtin_fmaf(xv, __uint_as_float(w[r][i]), acc[t][i]);
+                acc[t][i] = __builtin_fmaf(xv, __uint_as_float(w[j][i]), acc[t][i]);
+        }
+        // the wave's four row offsets (lanes e4, e4 + 16, e4 + 32, e4 + 48)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[t][i] += __shfl_xor(acc[t][i], 16, 64);
+            acc[t][i] += __shfl_xor(acc[t][i], 32, 64);
         }
     }
+    if (lane < 16) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_q[(wave * NT + t) * kMaxExperts + e0 + i] = acc[t][i];
+            for (int i = 0; i < 4; ++i) s_q[(wave * NT + t) * kRtExperts + 4 * e4 + i] = acc[t][i];
+    }
     __syncthreads();
-    for (int i = tid; i < T * E; i += 1024) {
-        const int t = i / E, e = i - t * E;
-        float v = 0.0f;
+    for (int i = tid; i < T * kRtExperts; i += kRtThreads) {
+        const int t = i / kRtExperts, el = i - t * kRtExperts, e = eb * kRtExperts + el;
+        if (e < E) {
+            float v = 0.0f;
 #pragma unroll
-        for (int q = 0; q < kRouterWaves; ++q) v += s_q[(q * NT + t) * kMaxExperts + e];
-        a.partial[((size_t)g * T + t) * E + e] = v;
+            for (int q = 0; q < 4; ++q) v += s_q[(q * NT + t) * kRtExperts + el];
+            a.partial[((size_t)rb * T + t) * E + e] = v;
+        }
     }
 }
 
@@ -343,93 +363,148 @@ __global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeA
     }
 }
 
-// One wave per NO outputs n (n = first + 8 o); lane covers 8 consecutive
-// intermediate k (one code word) of each 512-wide pass, for every slot.  All
-// slots' loads are issued before the arithmetic; the combine then adds
-// w_s * P_s in slot order and the shared expert last.  NO = 2 for larger T
-// (fewer, fuller work groups; at 4 the registers spill).
-template <int NO>
-__global__ __launch_bounds__(64 * kDownWaves) void decode_down_kernel(const DecodeArgs a) {
-    // token t = blockIdx.y: h of its k + 1 experts, staged once per work group
+// Down + combine for one token t = blockIdx.y and output rows n0 .. n0 + 7
+// (n0 = 8 blockIdx.x): the row tasks (output row, slot) -- slots 0..k-1 the
+// routed experts, slot k the shared expert -- go to 32 groups of 16 lanes
+// (task rt = group + 32 m); lane l of a group takes the 16-byte pieces
+// l, l + 16, .. (32 intermediate values each) of its task's weight row, so a
+// load instruction reads 64 contiguous bytes of each of four rows.  The
+// selected experts are loaded first, then the token's h (staged in LDS), then
+// every weight piece of the lane, all before any arithmetic.  Per task: the
+// lane's pieces in order, then a fixed DPP sum over the 16 lanes; the combine
+// adds w_s * P_s in slot order and the shared expert last.
+//   NM: tasks per lane group, ceil(8 (k + 1) / 32);  JP: pieces per lane per
+//   task, ceil(inter / 512).
+constexpr int kDnOutRows = 8;
+constexpr int kDnThreads = 512;
+constexpr int kDnStage = ((kMaxTopK + 1) * MOE_MAX_INTER / 8 + kDnThreads - 1) / kDnThreads;
+
+// Sum over each row of 16 lanes, left in every lane of the row (fixed order).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
+    v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
+    v += dpp_f32<0x141>(v);  // row_half_mirror
+    v += dpp_f32<0x140>(v);  // row_mirror
+    return v;
+}
+
+template <int NM, int JP>
+__global__ __launch_bounds__(kDnThreads) void decode_down_kernel(const DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_h[(kMaxTopK + 1) * MOE_MAX_INTER];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int I = a.I, k = a.k, d = a.d, t = blockIdx.y;
-    const u32x4* h_src = (const u32x4*)(a.h + (size_t)t * (k + 1) * I);
-    for (int i = tid; i < (k + 1) * I / 8; i += 64 * kDownWaves) ((u32x4*)s_h)[i] = h_src[i];
-    const int32_t* sel_idx = a.sel_idx + (size_t)t * k;
-    const float* sel_w = a.sel_w + (size_t)t * k;
-    __syncthreads();
-    const int n0 = blockIdx.x * kDownWaves * NO + (tid >> 6);
-    if (n0 >= d) return;
-    float part[NO][kMaxTopK + 1];
+    __shared__ float s_res[kDnOutRows * (kMaxTopK + 1)];
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int I = a.I, k = a.k, d = a.d, t = blockIdx.y, n0 = blockIdx.x * kDnOutRows;
+    const int K1 = k + 1, n_rt = kDnOutRows * K1, P = I / 32;
+    // 1. the experts of this lane's tasks
+    int ex[NM];
 #pragma unroll
-    for (int o = 0; o < NO; ++o)
+    for (int m = 0; m < NM; ++m) {
+        const int rt = grp + 32 * m;
+        const int s = rt < n_rt ? rt % K1 : 0;
+        ex[m] = a.sel_idx[(size_t)t * k + (s < k ? s : 0)];
+    }
+    // the combine's scores (threads 0..7, one output row each)
+    float wsc[kMaxTopK];
 #pragma unroll
-        for (int s = 0; s <= kMaxTopK; ++s) part[o][s] = 0.0f;
-    for (int jb = 0; jb < I; jb += 64 * 8) {
-        const int j0 = jb + 8 * lane;
-        const int jj = j0 < I ? j0 : 0;  // clamped, always valid; masked below
-        uint32_t q[NO][kMaxTopK + 1];
-        uint32_t sc[NO][kMaxTopK + 1], bi[NO][kMaxTopK + 1];
-        u32x4 hv[kMaxTopK + 1];
+    for (int s = 0; s < kMaxTopK; ++s) wsc[s] = a.sel_w[(size_t)t * k + (s < k ? s : 0)];
+    // 2. the token's h: (k + 1) x inter bf16, every load in flight at once
+    const int n_h = K1 * I / 8;
+    const u32x4* h_src = (const u32x4*)(a.h + (size_t)t * K1 * I);
+    u32x4 hv[kDnStage];
 #pragma unroll
-        for (int s = 0; s <= kMaxTopK; ++s) {
-            const int ss = s <= k ? s : k;  // slots past k repeat the shared expert (discarded)
-            const bool shared = ss == k;
-            const Q4 D = shared ? a.sh_down : a.down;
-            const size_t base = shared ? 0 : (size_t)sel_idx[ss] * d;
+    for (int u = 0; u < kDnStage; ++u) {
+        const int i = tid + kDnThreads * u;
+        hv[u] = h_src[i < n_h ? i : 0];
+    }
+    // 3. the weight pieces (clamped, always valid; invalid ones zeroed at use)
+    u32x4 q[NM][JP];
+    uint16_t sc[NM][JP], bi[NM][JP];
 #pragma unroll
-            for (int o = 0; o < NO; ++o) {
-                const int n = n0 + kDownWaves * o;
-                const size_t row = base + (n < d ? n : n0);  // clamped, always valid
-                q[o][s] = D.q[row * (I / 8) + jj / 8];
-                sc[o][s] = D.scale[row * (I / kGroup) + jj / kGroup];
-                bi[o][s] = D.bias[row * (I / kGroup) + jj / kGroup];
-            }
-            hv[s] = *(const u32x4*)(s_h + ss * I + jj);
+    for (int m = 0; m < NM; ++m) {
+        const int rt = grp + 32 * m;
+        const int rtc = rt < n_rt ? rt : 0;
+        const int nl = rtc / K1, s = rtc - nl * K1;
+        const bool sh = s == k;
+        const uint32_t* Wq = sh ? a.sh_down.q : a.down.q;
+        const uint16_t* Ws = sh ? a.sh_down.scale : a.down.scale;
+        const uint16_t* Wb = sh ? a.sh_down.bias : a.down.bias;
+        const size_t row = (sh ? 0 : (size_t)ex[m] * d) + n0 + nl;
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            const int pc = l16 + 16 * j;
+            const int pcc = pc < P ? pc : 0;
+            q[m][j] = *(const u32x4*)(Wq + row * (I / 8) + 4 * pcc);
+            sc[m][j] = Ws[row * (I / kGroup) + pcc / 2];
+            bi[m][j] = Wb[row * (I / kGroup) + pcc / 2];
         }
-#pragma unroll
-        for (int o = 0; o < NO; ++o)
-#pragma unroll
-            for (int s = 0; s <= kMaxTopK; ++s) {
-                const float p =
-                    dot8_bf16(q[o][s], dq_scale(sc[o][s]), bf16_to_f32(bi[o][s]), hv[s], 0.0f);
-                part[o][s] += j0 < I ? p : 0.0f;
-            }
     }
 #pragma unroll
-    for (int o = 0; o < NO; ++o) {
-        float y = 0.0f, sh = 0.0f;
+    for (int u = 0; u < kDnStage; ++u) {
+        const int i = tid + kDnThreads * u;
+        if (i < n_h) ((u32x4*)s_h)[i] = hv[u];
+    }
+    __syncthreads();
+    // 4. per task: the lane's pieces, then the 16-lane sum
 #pragma unroll
-        for (int s = 0; s <= kMaxTopK; ++s) {
-            if (s <= k) {
-                const float p = wave_sum_dpp(part[o][s]);
-                if (s < k) y += sel_w[s] * p;
-                else sh = p;
-            }
+    for (int m = 0; m < NM; ++m) {
+        const int rt = grp + 32 * m;
+        const int rtc = rt < n_rt ? rt : 0;
+        const int s = rtc % K1;
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+            const int pc = l16 + 16 * j;
+            const int pcc = pc < P ? pc : 0;
+            const u32x4* hp = (const u32x4*)(s_h + s * I + 32 * pcc);
+            const float s9 = dq_scale(sc[m][j]), b = bf16_to_f32(bi[m][j]);
+            float p = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) p = dot8_bf16(q[m][j][w], s9, b, hp[w], p);
+            acc += pc < P ? p : 0.0f;
         }
-        const int n = n0 + kDownWaves * o;
-        if (lane == 0 && n < d) a.y[(size_t)t * d + n] = f32_to_bf16(y + sh);
+        acc = row16_sum(acc);
+        if (l16 == 0 && rt < n_rt) s_res[rt] = acc;
+    }
+    __syncthreads();
+    // 5. the combine, one output row per thread
+    if (tid < kDnOutRows) {
+        float y = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+            if (s < k) y += wsc[s] * s_res[tid * K1 + s];
+        y += s_res[tid * K1 + k];
+        a.y[(size_t)t * d + n0 + tid] = f32_to_bf16(y);
     }
 }
 
 template <int NT>
-void launch_router_shared(const DecodeArgs& a, int n_part, int n_rows, hipStream_t s) {
+void launch_router_shared(const DecodeArgs& a, int n_router, hipStream_t s) {
     const int n_groups = (a.T + kSharedTokens - 1) / kSharedTokens;
-    const dim3 g1(n_part + n_rows * n_groups);
+    const int n_rows = (a.I + kSharedRowsPerGroup - 1) / kSharedRowsPerGroup;
+    const dim3 g1(n_router + n_rows * n_groups);
     if (a.E % 4 == 0)
-        hipLaunchKernelGGL((decode_router_shared_kernel<NT, true>), g1, dim3(1024), 0, s, a, n_part);
+        hipLaunchKernelGGL((decode_router_shared_kernel<NT, true>), g1, dim3(kRtThreads), 0, s, a,
+                           n_router);
     else
-        hipLaunchKernelGGL((decode_router_shared_kernel<NT, false>), g1, dim3(1024), 0, s, a, n_part);
+        hipLaunchKernelGGL((decode_router_shared_kernel<NT, false>), g1, dim3(kRtThreads), 0, s, a,
+                           n_router);
+}
+
+template <int NM>
+static void launch_down(const DecodeArgs& a, dim3 g3, hipStream_t s) {
+    if (a.I <= 512) hipLaunchKernelGGL((decode_down_kernel<NM, 1>), g3, dim3(kDnThreads), 0, s, a);
+    else if (a.I <= 1024) hipLaunchKernelGGL((decode_down_kernel<NM, 2>), g3, dim3(kDnThreads), 0, s, a);
+    else hipLaunchKernelGGL((decode_down_kernel<NM, 4>), g3, dim3(kDnThreads), 0, s, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     const int n_part = (a.d + kRouterRows - 1) / kRouterRows;
+    const int n_router = n_part * ((a.E + kRtExperts - 1) / kRtExperts);
     const int n_rows = (a.I + kDecRows - 1) / kDecRows;
-    if (a.T <= 1) launch_router_shared<1>(a, n_part, n_rows, s);
-    else if (a.T <= 2) launch_router_shared<2>(a, n_part, n_rows, s);
-    else if (a.T <= 4) launch_router_shared<4>(a, n_part, n_rows, s);
-    else launch_router_shared<8>(a, n_part, n_rows, s);
+    if (a.T <= 1) launch_router_shared<1>(a, n_router, s);
+    else if (a.T <= 2) launch_router_shared<2>(a, n_router, s);
+    else if (a.T <= 4) launch_router_shared<4>(a, n_router, s);
+    else launch_router_shared<8>(a, n_router, s);
     trace_point(s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -443,11 +518,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     trace_point(s);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // outputs per wave: about two work groups per CU in all
-    const int NO = ((a.d + kDownWaves - 1) / kDownWaves) * a.T > 512 ? 2 : 1;
-    const dim3 g3((a.d + kDownWaves * NO - 1) / (kDownWaves * NO), a.T);
-    if (NO == 1) hipLaunchKernelGGL(decode_down_kernel<1>, g3, dim3(64 * kDownWaves), 0, s, a);
-    else hipLaunchKernelGGL(decode_down_kernel<2>, g3, dim3(64 * kDownWaves), 0, s, a);
+    const dim3 g3(a.d / kDnOutRows, a.T);
+    const int n_rt = kDnOutRows * (a.k + 1);
+    if (n_rt <= 32) launch_down<1>(a, g3, s);
+    else if (n_rt <= 64) launch_down<2>(a, g3, s);
+    else launch_down<3>(a, g3, s);
     trace_point(s);
     return hipGetLastError();
 }

@@ -184,14 +184,33 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
+// Wave-wide reductions on the vector ALUs only: DPP within rows of 16 lanes,
+// then gfx950's row swaps (v_permlane16_swap: rows 0<->1, 2<->3;
+// v_permlane32_swap: lanes 0-31 <-> 32-63).  Every lane gets the result; no
+// scalar round trip.
+// ---------------------------------------------------------------------------
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(r16[0], r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(r32[0], r32[1]);
+}
+
+// ---------------------------------------------------------------------------
 // Top-k of one token's logits by one wave (E <= 256: lane l holds experts
 // l, l + 64, l + 128, l + 192).  Selection compares fp32 logits: larger
 // first, equal logits -> lower expert index.  Each of the k rounds takes the
-// wave maximum of the keys, finds the lowest expert holding it from four
-// ballots (scalar work) and retires that key.
+// wave maximum of the order keys, then the wave minimum of the expert indices
+// holding it, and retires that key (all on the vector ALUs).
 // Scores: softmax over the experts renormalised over the k selected ones,
-// computed as exp(l_s - l_max) / sum_s' exp(l_s' - l_max) (the full-softmax
-// normaliser cancels).  Lane s < k returns slot s.
+// computed as exp(l_s - l_max) / sum_s' exp(l_s' - l_max) with the sum taken
+// in slot order (the full-softmax normaliser cancels).  Lane s < k returns
+// slot s.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E, int k, int lane,
                                           int* out_e, float* out_w) {
@@ -199,47 +218,36 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? logit_key(lrow[e]) : 0u;
+        key[i] = e < E ? logit_key(lrow[e]) : 0u;  // key 0: no finite logit, never chosen
     }
+    auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+    auto umin = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
     float sel_l[kMaxTopK];
-    int sel_e[kMaxTopK];
+    int my_e = 0;
+    float my_l = 0.0f;
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) {
         sel_l[s] = 0.0f;
-        sel_e[s] = 0;
         if (s < k) {
-            const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-            const uint64_t b0 = __builtin_amdgcn_ballot_w64(key[0] == m);
-            const uint64_t b1 = __builtin_amdgcn_ballot_w64(key[1] == m);
-            const uint64_t b2 = __builtin_amdgcn_ballot_w64(key[2] == m);
-            const uint64_t b3 = __builtin_amdgcn_ballot_w64(key[3] == m);
-            const int e = b0 ? __builtin_ctzll(b0)
-                        : b1 ? 64 + __builtin_ctzll(b1)
-                        : b2 ? 128 + __builtin_ctzll(b2)
-                             : 192 + __builtin_ctzll(b3);
-            if ((e & 63) == lane) {
+            const uint32_t m = wave_reduce_u32(umax(umax(key[0], key[1]), umax(key[2], key[3])), umax);
+            uint32_t c = 0xFFFFu;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (i == (e >> 6)) key[i] = 0u;
-            }
-            sel_e[s] = e;
+            for (int i = 3; i >= 0; --i) c = key[i] == m ? (uint32_t)(64 * i + lane) : c;
+            const uint32_t e = wave_reduce_u32(c, umin);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(64 * i + lane) == e ? 0u : key[i];
             sel_l[s] = key_logit(m);
+            if (s == lane) {
+                my_e = (int)e;
+                my_l = sel_l[s];
+            }
         }
     }
-    float ex[kMaxTopK], sum = 0.0f;
+    float sum = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        ex[s] = s < k ? expf(sel_l[s] - sel_l[0]) : 0.0f;
-        sum += ex[s];
-    }
-    *out_e = 0;
-    *out_w = 0.0f;
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s)
-        if (s == lane) {
-            *out_e = sel_e[s];
-            *out_w = ex[s] / sum;
-        }
+    for (int s = 0; s < kMaxTopK; ++s) sum += s < k ? expf(sel_l[s] - sel_l[0]) : 0.0f;
+    *out_e = lane < k ? my_e : 0;
+    *out_w = lane < k ? expf(my_l - sel_l[0]) / sum : 0.0f;
 }
 
 }  // namespace q4moe
