@@ -105,7 +105,7 @@ def prefill_work(T, d, I, E, k, counts):
     }
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gate_up_T2048_decode.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_moe_layer_T2048_decode.md")
 KERNEL_SOURCES = ("q4_routed_expert_amd/csrc/prefill.hip", "q4_routed_expert_amd/csrc/decode.hip",
                   "q4_routed_expert_amd/csrc/q4moe_dev.h", "q4_routed_expert_amd/csrc/internal.h")
 LM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_lm_head_V248320.md")
@@ -189,6 +189,16 @@ def bench_prefill(args, q4, torch, ev, stream):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # clocks under load: sysfs read a few times while a queue of untimed steps runs
+    pci = gpu_pci(torch)
+    n_load = max(64, int(0.15e6 / 250))
+    for i in range(n_load):
+        step(i)
+    under_load = []
+    for _ in range(4):
+        time.sleep(0.02)
+        under_load.append(gpu_clocks(pci))
+    torch.cuda.synchronize()
     # timed steps: only two events around the whole loop
     K = args.steps
     t = ev.make(2)
@@ -228,6 +238,7 @@ def bench_prefill(args, q4, torch, ev, stream):
         "workload": w, "ms_per_step": ms_step, "wall_ms_per_step": wall / K * 1e3,
         "tok_s": w.T / sec, "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "gbps": work["bytes"] / sec / 1e9, "work": work, "kernel_us": {n: v * 1e3 for n, v in per.items()},
+        "clocks_under_load": under_load,
     }
     # two layer steps (route + prefill on each weight set) captured once in a
     # HIP graph and replayed; the output must equal the eager output
@@ -266,6 +277,106 @@ def bench_prefill(args, q4, torch, ev, stream):
     del layers, ws
     torch.cuda.empty_cache()
     return out
+
+
+def bench_config(name, args, q4, torch, ev, stream):
+    """route + prefill on one of the other prefill workloads (its own seed and, for
+    the skewed one, its router bias), two weight sets alternated (the second drawn
+    with seed + 100), timed like the headline."""
+    from workloads import WORKLOADS, make_layer
+    w = WORKLOADS[name]
+    log(f"config {name}: generating two weight sets (T={w.T}, d={w.d}, I={w.inter}, "
+        f"E={w.n_experts}, k={w.top_k}, seed {w.seed})")
+    L0, x = make_layer(w)
+    L1, _ = make_layer(dataclasses.replace(w, seed=w.seed + 100))
+    if w.skew:  # the same per-expert preference on both sets
+        L1["router_bias"] = L0["router_bias"]
+    dev = torch.device("cuda:0")
+    layers = [q4.DeviceLayer.from_host(L, dev) for L in (L0, L1)]
+    del L0, L1
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    r = q4.DeviceRouting(w.T, w.n_experts, w.top_k, dev)
+    ws = q4.workspace(layers[0], w.T, dev)
+    y = torch.empty((w.T, w.d), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        q4.route(layers[i % 2], xd, routing=r)
+        q4.prefill(layers[i % 2], xd, r, ws, y)
+
+    for i in range(max(20, args.warmup // 4)):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(10, args.steps)
+    t = ev.make(2)
+    ev.record(t[0], stream)
+    for i in range(n):
+        step(i)
+    ev.record(t[1], stream)
+    torch.cuda.synchronize()
+    us = ev.ms(t[0], t[1]) * 1e3 / n
+    work = prefill_work(w.T, w.d, w.inter, w.n_experts, w.top_k, r.counts.cpu().numpy())
+    sec = us * 1e-6
+    rec = {"T": w.T, "d": w.d, "inter": w.inter, "n_experts": w.n_experts, "top_k": w.top_k,
+           "seed": w.seed, "skewed_router": w.skew, "steps": n, "us_per_layer": round(us, 2),
+           "tok_s": round(w.T / sec, 1), "tflops": round(work["flops"] / sec / 1e12, 2),
+           "mfma_frac": round(work["flops"] / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "gbps": round(work["bytes"] / sec / 1e9, 1),
+           "hbm_frac": round(work["bytes"] / sec / 1e9 / PEAK_HBM_GBPS, 4),
+           "touched_experts": work["touched_experts"],
+           "algorithmic": {"flops": work["flops"], "bytes": work["bytes"]}}
+    log(f"config {name}: {us:.1f} us/layer, {rec['tok_s']:.0f} tok/s, MFMA {rec['mfma_frac']:.3f}, "
+        f"HBM {rec['hbm_frac']:.3f}, {rec['touched_experts']} experts touched")
+    del layers, ws, r, y
+    torch.cuda.empty_cache()
+    return rec
+
+
+def host_info():
+    """The host CPU model and thread counts (for the oracle's timing), from /proc
+    (no child process: the bench must not start programs once the GPU is in use)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def gpu_clocks(pci=None):
+    """The current shader and memory clock levels (the line marked '*' of
+    pp_dpm_sclk / pp_dpm_mclk in sysfs) of the GPU at PCI address prefix `pci`
+    ("dddd:bb:dd."), or of every GPU the kernel driver lists when it is None."""
+    import glob
+    cards = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        addr = os.path.basename(os.path.realpath(dev))
+        if pci is not None and not addr.startswith(pci):
+            continue
+        rec = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [ln.split(":", 1)[1].strip(" *\n") for ln in f if ln.rstrip().endswith("*")]
+                rec[name[7:]] = cur[0] if cur else None
+            except OSError:
+                pass
+        if rec:
+            cards[addr] = rec
+    return cards or {"error": "no pp_dpm_sclk in sysfs"}
+
+
+def gpu_pci(torch):
+    """PCI address prefix of cuda:0 as sysfs names it."""
+    p = torch.cuda.get_device_properties(0)
+    return f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}."
 
 
 def bench_decode(args, q4, torch, ev, stream):
@@ -401,13 +512,14 @@ def bench_decode(args, q4, torch, ev, stream):
             f"experts, {rec['gbps']:.0f} GB/s on their bytes, per kernel (us): " +
             ", ".join(f"{n}={v:.2f}" for n, v in zip(names, perT)))
         del rT
-    ex_bytes = expert_bytes
-    k_sec = sum(per.values()) / 1e6
-    out["roofline"] = {"bound": "hbm", "achieved": round(ex_bytes / k_sec / 1e9, 1),
+    # priced on the measured layer time (the three kernels back to back, launch
+    # gaps included), the same time as us_per_layer
+    out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1),
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": round(ex_bytes / k_sec / 1e9 / PEAK_HBM_GBPS, 4),
+                       "frac": round(gbps / PEAK_HBM_GBPS, 4),
                        "traffic": measured_traffic("decode_bytes_per_layer"),
-                       "kernels": "decode router partials + shared gate/up, top-k + routed gate/up, down/combine"}
+                       "kernels": "decode router partials + shared gate/up, top-k + routed gate/up, "
+                                  "down/combine (one layer call)"}
     del layers, ws
     torch.cuda.empty_cache()
     return out
@@ -571,7 +683,7 @@ def cpu_baseline(n_tokens):
     oracle.layer_tokens(L, xs, np.arange(n_tokens, dtype=np.int32), r["idx"], r["w"])
     sec = time.perf_counter() - t0
     return {"value": round(n_tokens / sec, 3), "unit": "tok/s", "cores": oracle.threads(),
-            "kind": "oracle", "seconds": round(sec, 2),
+            "kind": "oracle", "seconds": round(sec, 2), "host": host_info(),
             "sample": f"first {n_tokens} tokens of the prefill T=2048 layer: router logits, "
                       f"routing and all {w.top_k}+1 expert FFNs of those tokens (fp64 oracle)"}
 
@@ -597,6 +709,8 @@ def main():
                     help="skip the few-token decode figures (T = 2, 4, 8)")
     ap.add_argument("--sweep", default=None, metavar="T1,T2,...",
                     help="only the prefill sweep over these chunk sizes (balanced and skewed)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads (tiny, T=512, skewed T=4096)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB copy (for HBM byte-counter calibration)")
     args = ap.parse_args()
@@ -624,7 +738,11 @@ def main():
                                                  "top-8 + 1 shared, Q4 group-64, 2 weight sets"},
                           "sweep": rows}), flush=True)
         return
+    pci = gpu_pci(torch)
+    clocks_before = gpu_clocks(pci)
     pre = bench_prefill(args, q4, torch, ev, stream)
+    configs = {} if args.no_configs else {
+        n: bench_config(n, args, q4, torch, ev, stream) for n in ("tiny", "prefill512", "skew4096")}
     dec = None if args.no_decode else bench_decode(args, q4, torch, ev, stream)
     hand = None if args.no_handoff else bench_handoff(args, q4, torch, ev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
@@ -663,9 +781,13 @@ def main():
                                        for k, v in dec["graph"].items()}
         line["decode"]["tokens"] = dec["tokens"]
         line["roofline_decode"] = dec["roofline"]
+    if configs:
+        line["configs"] = configs
     if hand is not None:
         line["handoff"] = {k: v for k, v in hand.items() if k != "roofline"}
         line["roofline_handoff"] = hand["roofline"]
+    line["clocks"] = {"idle_before": clocks_before, "under_load": pre["clocks_under_load"],
+                      "idle_after": gpu_clocks(pci)}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
