@@ -671,6 +671,75 @@ def bench_sweep(args, q4, torch, ev, stream):
     return rows
 
 
+def bench_item_rows(args, q4, torch, ev, stream):
+    """Gate/up work-item height ablation: route + prefill at item heights 128, 64
+    and 32 rows (the rows that share one dequantised weight tile), T = 512, 2048,
+    4096, with the balanced router and with the skewed workload's router bias.
+    Weights: the T=2048 workload's two sets, alternated; x: the first T rows of one
+    seeded draw of 4096 rows; the skewed rows add the skewed workload's bias."""
+    from workloads import WORKLOADS, make_layer, skew_bias
+    base = WORKLOADS["prefill2048"]
+    Ts = (512, 2048, 4096)
+    w = dataclasses.replace(base, T=max(Ts))
+    log(f"item-height ablation: generating two weight sets and x for T up to {w.T}")
+    L0, x = make_layer(w)
+    L1, _ = make_layer(dataclasses.replace(w, seed=w.seed + 100))
+    bias = skew_bias(np.random.Generator(np.random.PCG64(WORKLOADS["skew4096"].seed)), w.n_experts)
+    dev = torch.device("cuda:0")
+    sets = {False: [q4.DeviceLayer.from_host(L, dev) for L in (L0, L1)],
+            True: [q4.DeviceLayer.from_host(dict(L, router_bias=bias), dev) for L in (L0, L1)]}
+    del L0, L1
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = q4.workspace(sets[False][0], w.T, dev)
+    lib = q4._abi.lib()
+    rows = []
+    for skew in (False, True):
+        for T in Ts:
+            r = q4.DeviceRouting(T, w.n_experts, w.top_k, dev)
+            y = torch.empty((T, w.d), dtype=torch.bfloat16, device=dev)
+            xs = xd[:T]
+            rec = {"T": T, "skew": skew}
+            # two passes in opposite orders, the faster kept (clock ramps and
+            # order effects cancel)
+            for m in (128, 64, 32, 32, 64, 128):
+                def step(i, tr=None):
+                    q4.route(sets[skew][i % 2], xs, routing=r)
+                    if tr is not None:
+                        lib.moe_trace_events(C.cast(tr, C.c_void_p), 4)
+                    q4.prefill(sets[skew][i % 2], xs, r, ws, y, item_rows=m)
+                    lib.moe_trace_events(None, 0)
+
+                for i in range(4):
+                    step(i)
+                torch.cuda.synchronize()
+                n = max(10, min(args.steps, 30))
+                t = ev.make(2)
+                ev.record(t[0], stream)
+                for i in range(n):
+                    step(i)
+                ev.record(t[1], stream)
+                torch.cuda.synchronize()
+                us = ev.ms(t[0], t[1]) * 1e3 / n
+                trs = [ev.make(4) for _ in range(8)]
+                for i, tr in enumerate(trs):
+                    step(i, tr)
+                torch.cuda.synchronize()
+                gu = sum(ev.ms(tr[0], tr[1]) for tr in trs) * 1e3 / len(trs)
+                prev = rec.get(f"rows{m}")
+                if prev is None or us < prev["us_per_layer"]:
+                    rec[f"rows{m}"] = {"us_per_layer": round(us, 2),
+                                       "tok_s": round(T / (us * 1e-6), 1), "gate_up_us": round(gu, 2)}
+            rec["touched_experts"] = int((r.counts.cpu().numpy() > 0).sum())
+            rows.append(rec)
+            log(f"item rows T={T} skew={skew}: " + ", ".join(
+                f"{m} rows {rec[f'rows{m}']['us_per_layer']:.1f} us/layer "
+                f"(gate/up {rec[f'rows{m}']['gate_up_us']:.1f})" for m in (128, 64, 32)))
+            del r, y
+    del sets, ws
+    torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(n_tokens):
     import oracle
     from workloads import WORKLOADS, make_layer
@@ -709,6 +778,8 @@ def main():
                     help="skip the few-token decode figures (T = 2, 4, 8)")
     ap.add_argument("--sweep", default=None, metavar="T1,T2,...",
                     help="only the prefill sweep over these chunk sizes (balanced and skewed)")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the gate/up item-height ablation (128 / 64 / 32 rows)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other prefill workloads (tiny, T=512, skewed T=4096)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -743,6 +814,7 @@ def main():
     pre = bench_prefill(args, q4, torch, ev, stream)
     configs = {} if args.no_configs else {
         n: bench_config(n, args, q4, torch, ev, stream) for n in ("tiny", "prefill512", "skew4096")}
+    abl = None if args.no_ablation else bench_item_rows(args, q4, torch, ev, stream)
     dec = None if args.no_decode else bench_decode(args, q4, torch, ev, stream)
     hand = None if args.no_handoff else bench_handoff(args, q4, torch, ev, stream)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_tokens)
@@ -783,6 +855,8 @@ def main():
         line["roofline_decode"] = dec["roofline"]
     if configs:
         line["configs"] = configs
+    if abl is not None:
+        line["sweep"] = {"gate_up_item_rows": abl}
     if hand is not None:
         line["handoff"] = {k: v for k, v in hand.items() if k != "roofline"}
         line["roofline_handoff"] = hand["roofline"]

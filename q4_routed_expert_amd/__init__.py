@@ -156,9 +156,16 @@ def route(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting | None = N
     return r
 
 
+_ITEM_ROWS_FLAGS = {128: 0, 64: _abi.MOE_ITEM_ROWS_64, 32: _abi.MOE_ITEM_ROWS_32}
+
+
 def prefill(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting,
             ws: torch.Tensor | None = None, y: torch.Tensor | None = None,
-            stream=None) -> torch.Tensor:
+            stream=None, item_rows: int = 128) -> torch.Tensor:
+    """moe_prefill (item_rows = 128) or moe_prefill_ex with the gate/up work-item
+    height item_rows (64 or 32)."""
+    if item_rows not in _ITEM_ROWS_FLAGS:
+        raise ValueError(f"item_rows must be one of 128, 64, 32, not {item_rows}")
     T = x.shape[0]
     if ws is None:
         ws = workspace(layer, T, x.device)
@@ -168,9 +175,16 @@ def prefill(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting,
     _need(y, "y", torch.bfloat16, T * layer.d)
     _need(routing.perm, "routing.perm", torch.int32, T * layer.top_k)
     _on_gpu(x=x, y=y, ws=ws, perm=routing.perm)
-    _check(_abi.lib().moe_prefill(C.addressof(layer.struct), _ptr(x), T, C.addressof(routing.struct),
-                                  _ptr(ws), ws.numel(), _ptr(y), _stream(stream)),
-           "moe_prefill")
+    if item_rows == 128:
+        _check(_abi.lib().moe_prefill(C.addressof(layer.struct), _ptr(x), T,
+                                      C.addressof(routing.struct), _ptr(ws), ws.numel(), _ptr(y),
+                                      _stream(stream)),
+               "moe_prefill")
+    else:
+        _check(_abi.lib().moe_prefill_ex(C.addressof(layer.struct), _ptr(x), T,
+                                         C.addressof(routing.struct), _ptr(ws), ws.numel(),
+                                         _ptr(y), _ITEM_ROWS_FLAGS[item_rows], _stream(stream)),
+               "moe_prefill_ex")
     return y
 
 

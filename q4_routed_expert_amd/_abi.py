@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4moe.so
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_LOGITS_IN = 1
+MOE_ITEM_ROWS_64, MOE_ITEM_ROWS_32 = 2, 4
 MOE_BLOCK_ROWS = 32
 MOE_TILE_ROWS = 128
 MOE_ROUTE_BLOCK = 256
@@ -18,7 +19,8 @@ MOE_STATIC_SCRATCH_BYTES = 1 << 20
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_TOKENS, MOE_MAX_D, MOE_MAX_INTER = 256, 8, 32768, 8192, 2048
 
 # every function include/q4moe.h declares
-EXPORTS = ("moe_block_map_capacity", "moe_workspace_bytes", "moe_route", "moe_prefill", "moe_trace_events",
+EXPORTS = ("moe_block_map_capacity", "moe_workspace_bytes", "moe_route", "moe_prefill",
+           "moe_prefill_ex", "moe_trace_events",
            "moe_decode", "moe_decode_tokens", "moe_dequant", "moe_strerror", "moe_last_error",
            "moe_lm_workspace_bytes", "moe_lm_argmax", "moe_decode_tokens_static")
 
@@ -69,6 +71,7 @@ def lib():
         L.moe_workspace_bytes.restype = C.c_size_t
         L.moe_route.argtypes = [vp, vp, i32, C.c_uint32, vp, vp]
         L.moe_prefill.argtypes = [vp, vp, i32, vp, vp, C.c_size_t, vp, vp]
+        L.moe_prefill_ex.argtypes = [vp, vp, i32, vp, vp, C.c_size_t, vp, C.c_uint32, vp]
         L.moe_decode.argtypes = [vp, vp, C.c_uint32, vp, vp, C.c_size_t, vp, vp]
         L.moe_decode_tokens.argtypes = [vp, vp, i32, C.c_uint32, vp, vp, C.c_size_t, vp, vp]
         L.moe_decode_tokens_static.argtypes = [vp, vp, i32, C.c_uint32, vp, vp, vp]
@@ -76,7 +79,7 @@ def lib():
         L.moe_lm_workspace_bytes.argtypes = [vp]
         L.moe_lm_workspace_bytes.restype = C.c_size_t
         L.moe_lm_argmax.argtypes = [vp, vp, C.c_uint32, vp, vp, vp, vp, C.c_size_t, vp]
-        for f in ("moe_route", "moe_prefill", "moe_decode", "moe_decode_tokens", "moe_dequant",
+        for f in ("moe_route", "moe_prefill", "moe_prefill_ex", "moe_decode", "moe_decode_tokens", "moe_dequant",
                   "moe_lm_argmax", "moe_decode_tokens_static"):
             getattr(L, f).restype = C.c_int
         L.moe_trace_events.argtypes = [vp, i32]

@@ -209,10 +209,18 @@ int moe_route(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t flags,
 
 int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r, void* ws,
                 size_t ws_bytes, uint16_t* y, void* stream) {
+    return moe_prefill_ex(L, x, T, r, ws, ws_bytes, y, 0u, stream);
+}
+
+int moe_prefill_ex(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r,
+                   void* ws, size_t ws_bytes, uint16_t* y, uint32_t flags, void* stream) {
     int rc;
     if ((rc = check_layer(L)) || (rc = check_tokens(T)) || (rc = check_routing(r)) ||
         (rc = check_ptr(x, "x")) || (rc = check_ptr(y, "y")) || (rc = check_ptr(ws, "workspace")))
         return rc;
+    if ((flags & ~(MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32)) ||
+        (flags & (MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32)) == (MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32))
+        return fail(MOE_EINVAL, "prefill flags 0x%x", flags);
     const size_t need = moe_workspace_bytes(L, T);
     if (ws_bytes < need)
         return fail(MOE_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -237,6 +245,7 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
     a.n_tiles = r->n_tiles;
     a.topk_w = r->topk_w;
     a.tile_bound = moe_block_map_capacity(T, L->top_k, L->n_experts, MOE_TILE_ROWS);
+    a.item_sh = (flags & MOE_ITEM_ROWS_32) ? 2 : (flags & MOE_ITEM_ROWS_64) ? 1 : 0;
     a.h = (uint16_t*)(base + pw.h);
     a.h_sh = (uint16_t*)(base + pw.h_sh);
     a.part = (uint16_t*)(base + pw.part);

@@ -908,6 +908,18 @@ constexpr int kGuPer = (kGuMaxItems + kGuThreads - 1) / kGuThreads;
 __device__ __forceinline__ int gu_unit_cost(int ms) { return 2 + ms; }
 constexpr int kGuRunMax = 512;  // items one group may hold (s_items)
 
+// Routed item i of the gate/up kernel: part i % S of 128-row tile i / S of the
+// tile map (S = 1 << item_sh parts of 128 >> item_sh rows each).  Returns its
+// expert, first row and row count; M <= 0 for a part past the expert's rows.
+__device__ __forceinline__ void gu_routed_item(const PrefillArgs& a, int i, int& e, int& row0,
+                                               int& M) {
+    const int rows = kMT >> a.item_sh;
+    const int t = i >> a.item_sh, part = i & ((1 << a.item_sh) - 1);
+    e = a.tile_map[2 * t];
+    row0 = a.tile_map[2 * t + 1] + part * rows;
+    M = min(rows, a.offsets[e + 1] - row0);
+}
+
 __device__ __forceinline__ int item_run(const PrefillArgs& a, int n_tiles, int n_items, int Q,
                                         int q, int* s_items) {
     __shared__ int s_cls[2][kGuWaves];  // per-wave class counts, 16 bits per class
@@ -923,11 +935,12 @@ __device__ __forceinline__ int item_run(const PrefillArgs& a, int n_tiles, int n
         if (r < R && i < n_items) {
             int M;
             if (i < n_tiles) {
-                const int e = a.tile_map[2 * i], r0 = a.tile_map[2 * i + 1];
-                M = min(kMT, a.offsets[e + 1] - r0);
+                int e, r0;
+                gu_routed_item(a, i, e, r0, M);
             } else {
                 M = min(kGuShRows, a.T - (i - n_tiles) * kGuShRows);
             }
+            if (M <= 0) continue;  // an empty part of a tile: no unit
             const int c = (M + 31) / 32 - 1;
             cls[r] = c;
             const int one = 1 << (16 * (c & 1));
@@ -1031,7 +1044,7 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int G = gridDim.x, g = blockIdx.x;
     const int K = a.d, Nw = a.I;
-    const int n_tiles = *a.n_tiles;
+    const int n_tiles = *a.n_tiles << a.item_sh;  // routed items
     const int sh_items = (a.T + kGuShRows - 1) / kGuShRows;
     const int n_items = n_tiles + sh_items;
     const int NL = ((K + kKC - 1) / kKC + kStages - 1) / kStages * kStages;  // chunks per unit
@@ -1069,7 +1082,7 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     // rows) and every group carries about the same work.  Otherwise (a grid
     // that does not split so): the round-robin list below.
     const int gpx = (G / 8) / n_cb;  // groups per XCD
-    const bool grouped = kGuGrouped && G % 8 == 0 && gpx > 0 &&
+    const bool grouped = kGuGrouped && G % 8 == 0 && gpx > 0 && n_items <= kGuPer * kGuThreads &&
                          (long long)n_items <= (long long)kGuRunMax * 8 * gpx / 4;
     __shared__ int s_items[kGuRunMax];
     int i_next = 0, i_end = 0, my_cb = 0;
@@ -1096,17 +1109,16 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 u_next += G;
                 if (item >= n_items) continue;
             }
-            const int bi = nb++;
             int e = 0, row0, M, shared = 0;
             if (item < n_tiles) {
-                e = a.tile_map[2 * item];
-                row0 = a.tile_map[2 * item + 1];
-                M = min(kMT, a.offsets[e + 1] - row0);
+                gu_routed_item(a, item, e, row0, M);
+                if (M <= 0) continue;  // uniform: an empty part of a tile
             } else {
                 shared = 1;
                 row0 = (item - n_tiles) * kGuShRows;
                 M = min(kGuShRows, a.T - row0);
             }
+            const int bi = nb++;
             if (tid == 0) s_unit[bi] = UnitDesc{e, row0, M, cb, shared};
             if (tid < kMT) {
                 int src = 0, dst = -1;

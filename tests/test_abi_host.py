@@ -37,7 +37,7 @@ def test_header_limits_match_binding():
     for name in ("MOE_GROUP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_TOKENS", "MOE_MAX_D",
                  "MOE_MAX_INTER", "MOE_BLOCK_ROWS", "MOE_TILE_ROWS", "MOE_ROUTE_BLOCK",
                  "MOE_DECODE_ROUTER_ROWS", "MOE_MAX_DECODE_TOKENS", "MOE_LOGITS_IN",
-                 "MOE_MAX_VOCAB"):
+                 "MOE_MAX_VOCAB", "MOE_ITEM_ROWS_64", "MOE_ITEM_ROWS_32"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m, name
         if hasattr(_abi, name):
@@ -114,6 +114,21 @@ def test_prefill_checks_workspace_size_before_launch():
     assert rc == _abi.MOE_EWORKSPACE
     rc = lib.moe_decode(C.addressof(L), FAKE, _abi.MOE_LOGITS_IN, None, FAKE, 1 << 30, FAKE, None)
     assert rc == _abi.MOE_EINVAL
+
+
+def test_prefill_ex_checks_flags_before_launch():
+    lib = _abi.lib()
+    L = _layer()
+    need = lib.moe_workspace_bytes(C.addressof(L), 2048)
+    r = _routing()
+    call = lambda flags, ws=need: lib.moe_prefill_ex(C.addressof(L), FAKE, 2048, C.addressof(r),
+                                                     FAKE, ws, FAKE, flags, None)
+    assert call(_abi.MOE_ITEM_ROWS_64 | _abi.MOE_ITEM_ROWS_32) == _abi.MOE_EINVAL
+    assert call(1) == _abi.MOE_EINVAL
+    assert call(8) == _abi.MOE_EINVAL
+    # valid flags get as far as the workspace check
+    for flags in (0, _abi.MOE_ITEM_ROWS_64, _abi.MOE_ITEM_ROWS_32):
+        assert call(flags, need - 1) == _abi.MOE_EWORKSPACE
 
 
 @pytest.mark.parametrize("T,code", [(0, _abi.MOE_EUNSUPPORTED), (-1, _abi.MOE_EUNSUPPORTED),

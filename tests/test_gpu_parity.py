@@ -350,6 +350,44 @@ def test_gate_up_round_robin_schedule(dev):
     run_layer_case(L, x, dev, "items", "round-robin gate/up", items=300)
 
 
+@pytest.mark.parametrize("T,d,inter,E,k,bias,seed", [
+    (600, 256, 128, 4, 2, False, 3),     # several 128-row tiles per expert, ragged tails
+    (300, 512, 512, 16, 4, True, 11),    # the resident down GEMM after gate/up
+    (100, 256, 128, 256, 8, False, 5),   # most experts empty: most parts of tiles empty
+    (20000, 64, 512, 256, 8, True, 14),  # at 32-row items more items than the grouped
+                                         # schedule takes: the round-robin unit list
+])
+def test_item_rows_variants(T, d, inter, E, k, bias, seed, dev):
+    # the gate/up work item at 64 and 32 rows: every row's products are
+    # accumulated in the same order as at 128 rows, so y is bit-identical; the
+    # 32-row run is also compared with the oracle
+    rng = np.random.default_rng(2000 + seed)
+    L = random_layer(rng, d, inter, E, k, router_bias=bias)
+    x = random_x(rng, T, d)
+    layer = q4.DeviceLayer.from_host(L, dev)
+    xd = xdev(x, dev)
+    l_ref = oracle.router_logits(x, L["w_router"], L.get("router_bias"))
+    ref, bm, tm = oracle_routing(l_ref, k)
+    r = q4.DeviceRouting(T, E, k, dev)
+    r.logits.copy_(torch.from_numpy(l_ref))
+    q4.route(layer, xd, routing=r, logits_in=True)
+    compare_routing(r, ref, T, E, k, bm, tm)
+    n_items32 = 4 * int(r.n_tiles.cpu()[0]) + (T + 63) // 64
+    ws = q4.workspace(layer, T, dev)
+    ys = {m: host_bits(q4.prefill(layer, xd, r, ws, item_rows=m)) for m in (128, 64, 32)}
+    torch.cuda.synchronize()
+    for m in (64, 32):
+        assert np.array_equal(ys[m], ys[128]), f"item_rows={m} differs from 128"
+    tokens = np.arange(T, dtype=np.int32) if T <= 600 else item_tokens(ref, T, k)
+    y_exact, _ = oracle.layer_tokens(L, x, tokens, ref["idx"], ref["w"])
+    err, rms, worst = y_error(ys[32][tokens], y_exact)
+    log(f"item rows T={T} E={E} k={k}: 32-row items ({n_items32} gate/up items), y max "
+        f"err/rms={err:.3e}, worst err/allowed={worst:.3f} ({len(tokens)} tokens)")
+    assert worst <= 1.0
+    with pytest.raises(ValueError):
+        q4.prefill(layer, xd, r, ws, item_rows=16)
+
+
 def test_prefill_at_the_token_limit(dev):
     # T = 32768 (the limit): more gate/up items than one thread of the
     # schedule's 512 covers five at a time; every work item compared
