@@ -909,23 +909,44 @@ __device__ __forceinline__ int gu_unit_cost(int ms) { return 2 + ms; }
 constexpr int kGuRunMax = 512;  // items one group may hold (s_items)
 
 // Routed item i of the gate/up kernel: part i % S of 128-row tile i / S of the
-// tile map (S = 1 << item_sh parts of 128 >> item_sh rows each).  Returns its
-// expert, first row and row count; M <= 0 for a part past the expert's rows.
-__device__ __forceinline__ void gu_routed_item(const PrefillArgs& a, int i, int& e, int& row0,
-                                               int& M) {
+// tile map (S = 1 << item_sh parts of 128 >> item_sh rows each).  Its rows end
+// where the next tile starts: the next tile of the same expert is 128 rows on,
+// and the next non-empty expert's rows follow the expert's last row directly
+// (the last tile ends at T * k).  So the row count needs only the tile map,
+// whose three entries load at once.  n_raw: tiles in the map; M <= 0 for a
+// part past the expert's rows.
+__device__ __forceinline__ void gu_tile_entries(const PrefillArgs& a, int t, int& e, int& r0,
+                                                int& nx) {
+    const int tc = min(t, a.tile_bound - 1), tn = min(t + 1, a.tile_bound - 1);  // valid entries
+    e = a.tile_map[2 * tc];
+    r0 = a.tile_map[2 * tc + 1];
+    nx = a.tile_map[2 * tn + 1];
+}
+__device__ __forceinline__ void gu_item_rows(const PrefillArgs& a, int i, int n_raw, int r0,
+                                             int nx, int& row0, int& M) {
     const int rows = kMT >> a.item_sh;
     const int t = i >> a.item_sh, part = i & ((1 << a.item_sh) - 1);
-    e = a.tile_map[2 * t];
-    row0 = a.tile_map[2 * t + 1] + part * rows;
-    M = min(rows, a.offsets[e + 1] - row0);
+    const int end = t + 1 < n_raw ? nx : a.T * a.k;
+    row0 = r0 + part * rows;
+    M = min(rows, end - row0);
 }
 
-__device__ __forceinline__ int item_run(const PrefillArgs& a, int n_tiles, int n_items, int Q,
-                                        int q, int* s_items) {
+// Items of the gate/up kernel at most, by the host's bound on the tile count.
+__device__ __forceinline__ int gu_item_bound(const PrefillArgs& a) {
+    return (a.tile_bound << a.item_sh) + (a.T + kGuShRows - 1) / kGuShRows;
+}
+
+__device__ __forceinline__ int item_run(const PrefillArgs& a, int n_raw, int n_tiles, int n_items,
+                                        int Q, int q, int* s_items) {
     __shared__ int s_cls[2][kGuWaves];  // per-wave class counts, 16 bits per class
     __shared__ int s_cnt[2][kGuWaves];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int R = (n_items + kGuThreads - 1) / kGuThreads;
+    // items per thread from the host bound, so that the tile-map loads below
+    // need not wait for the tile count
+    const int R = (gu_item_bound(a) + kGuThreads - 1) / kGuThreads;
+    int te[kGuPer], tr0[kGuPer], tnx[kGuPer];
+#pragma unroll
+    for (int r = 0; r < kGuPer; ++r) gu_tile_entries(a, (tid * R + r) >> a.item_sh, te[r], tr0[r], tnx[r]);
     int cls[kGuPer];  // subtile count - 1 of each of this thread's items (-1: none)
     int lo = 0, hi = 0;  // class counts: lo = classes 0, 1; hi = classes 2, 3
 #pragma unroll
@@ -935,8 +956,8 @@ __device__ __forceinline__ int item_run(const PrefillArgs& a, int n_tiles, int n
         if (r < R && i < n_items) {
             int M;
             if (i < n_tiles) {
-                int e, r0;
-                gu_routed_item(a, i, e, r0, M);
+                int r0;
+                gu_item_rows(a, i, n_raw, tr0[r], tnx[r], r0, M);
             } else {
                 M = min(kGuShRows, a.T - (i - n_tiles) * kGuShRows);
             }
@@ -1044,7 +1065,8 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
     const int G = gridDim.x, g = blockIdx.x;
     const int K = a.d, Nw = a.I;
-    const int n_tiles = *a.n_tiles << a.item_sh;  // routed items
+    const int n_raw = *a.n_tiles;                 // 128-row tiles in the map
+    const int n_tiles = n_raw << a.item_sh;       // routed items
     const int sh_items = (a.T + kGuShRows - 1) / kGuShRows;
     const int n_items = n_tiles + sh_items;
     const int NL = ((K + kKC - 1) / kKC + kStages - 1) / kStages * kStages;  // chunks per unit
@@ -1082,15 +1104,18 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     // rows) and every group carries about the same work.  Otherwise (a grid
     // that does not split so): the round-robin list below.
     const int gpx = (G / 8) / n_cb;  // groups per XCD
-    const bool grouped = kGuGrouped && G % 8 == 0 && gpx > 0 && n_items <= kGuPer * kGuThreads &&
-                         (long long)n_items <= (long long)kGuRunMax * 8 * gpx / 4;
+    // decided from the host's item bound alone, so that the schedule's loads
+    // can go out together with the tile count's
+    const int n_bound = gu_item_bound(a);
+    const bool grouped = kGuGrouped && G % 8 == 0 && gpx > 0 && n_bound <= kGuPer * kGuThreads &&
+                         (long long)n_bound <= (long long)kGuRunMax * 8 * gpx / 4;
     __shared__ int s_items[kGuRunMax];
     int i_next = 0, i_end = 0, my_cb = 0;
     if (grouped) {
         const int x = g % 8, j = g / 8;
         if (j >= gpx * n_cb) return;  // uniform: no group for this work group
         my_cb = j % n_cb;
-        i_end = item_run(a, n_tiles, n_items, 8 * gpx, x * gpx + j / n_cb, s_items);
+        i_end = item_run(a, n_raw, n_tiles, n_items, 8 * gpx, x * gpx + j / n_cb, s_items);
     }
     int u_next = g;
     while (true) {
@@ -1111,7 +1136,9 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
             }
             int e = 0, row0, M, shared = 0;
             if (item < n_tiles) {
-                gu_routed_item(a, item, e, row0, M);
+                int r0, nx;
+                gu_tile_entries(a, item >> a.item_sh, e, r0, nx);
+                gu_item_rows(a, item, n_raw, r0, nx, row0, M);
                 if (M <= 0) continue;  // uniform: an empty part of a tile
             } else {
                 shared = 1;
