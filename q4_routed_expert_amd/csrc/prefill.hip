@@ -1193,8 +1193,11 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
                 for (int p = 0; p < kGuALoads; ++p)
                     a_row[p] = (uint32_t)s_src[bb][(tid + kGuThreads * p) >> 4] * (uint32_t)K;
             }
-            const int kc = c * kKC;
-            return kc < K ? (uint32_t)(kc + 8 * a_lslot) : (uint32_t)((8 * a_lslot) & 63);
+            // a piece at or past K (a chunk past K, or the second half of a
+            // chunk that ends at K + 64) reads a column of the same row below
+            // 64 instead; its weights are zero
+            const uint32_t col = (uint32_t)(c * kKC + 8 * a_lslot);
+            return col < (uint32_t)K ? col : (uint32_t)((8 * a_lslot) & 63);
         };
         // direct-to-LDS load of rows 32p + 4 * wave .. +3 of an activation chunk
         auto dma_a = [&](auto buf_tag, uint32_t col, int p) {

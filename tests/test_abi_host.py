@@ -191,6 +191,24 @@ def test_router_loads_stay_inside_their_k_slice():
                         assert kk == k + 8 * half
 
 
+def test_gate_up_activation_pieces_stay_inside_their_row():
+    # The gate/up kernel stages 128-column chunks of gathered x rows, 16 bytes
+    # (8 columns) per lane at logical slot s of the chunk; the pipeline runs
+    # whole four-chunk groups, so chunks may lie partly or wholly past K.  For
+    # every d the ABI accepts, every piece read lies inside its row of x, and
+    # every piece inside K is read from where it is used.
+    for d in range(64, _abi.MOE_MAX_D + 1, 64):
+        n_chunks = -(-d // 128)
+        n_run = -(-n_chunks // 4) * 4
+        for c in range(n_run):
+            for slot in range(16):
+                col = c * 128 + 8 * slot
+                got = col if col < d else (8 * slot) & 63
+                assert 0 <= got and got + 8 <= d, (d, c, slot)
+                if col < d:
+                    assert got == col
+
+
 def test_static_scratch_decode_validates_before_launch():
     lib = _abi.lib()
     L = _layer()
