@@ -1073,6 +1073,14 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
     const bool pair_sb = (K / kGroup) % 2 == 0;  // scale/bias pairs are 4-byte aligned
     const bool is_up = (lane & 16) != 0;         // weight row lane%32: gate j0+n or up j0+n-16
     const int jrow = lane & 15;
+    // x as a raw buffer (T * d * 2 bytes < 2^32 by the size limits): the
+    // activation loads go direct to LDS as buffer loads.  The global (flat)
+    // form of the same load leaves the compiler unable to order it against
+    // the weight loads in the vector memory counter, and it then waits for
+    // every outstanding load before the first use of any loaded register;
+    // the buffer form keeps those waits exact.
+    const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.x, 0, (int)((uint32_t)a.T * (uint32_t)K * 2u), 0x00020000);
 
     f32x16 acc[4];
     WChunk bst[kStages];
@@ -1200,10 +1208,11 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
             return col < (uint32_t)K ? col : (uint32_t)((8 * a_lslot) & 63);
         };
         // direct-to-LDS load of rows 32p + 4 * wave .. +3 of an activation chunk
+        // (buffer form: see x_rsrc)
         auto dma_a = [&](auto buf_tag, uint32_t col, int p) {
             unsigned char* dst = tile_of(buf_tag) + (32 * p + 4 * wave) * kRowBytes;
-            __builtin_amdgcn_global_load_lds((const void*)(a.x + (a_row[p] + col)),
-                                             (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (__attribute__((address_space(3))) void*)dst,
+                                                     16, (a_row[p] + col) * 2u, 0, 0, 0);
         };
         auto w_refresh = [&](int bb, int c) {
             clamp_pos(bb, c);
@@ -1351,9 +1360,9 @@ __global__ __launch_bounds__(kGuThreads) void gate_up_kernel(const PrefillArgs a
         // final four from the second chunk on belong to the next unit (all
         // four loads: that unit's subtile count is not known here).
         //
-        // The compiler does not wait for direct-to-LDS loads before LDS reads,
-        // so each wave waits for its own loads of chunk c explicitly before
-        // the barrier that publishes the chunk: vmcnt(N), N = the vector
+        // A wave's reads of chunk c need every wave's loads of it, so each wave
+        // waits for its own loads of chunk c explicitly before the barrier
+        // that publishes the chunk: vmcnt(N), N = the vector
         // memory operations this wave issued after them, counted from the
         // fixed issue order below (a lower bound where it is not known, which
         // only waits longer).
