@@ -130,14 +130,16 @@ __device__ __forceinline__ void routed_store(const PrefillArgs& a, int dst, int 
     const int e = part_exp(pair_absmax(acc));
     if (half == 0) a.pexp[part_exp_index(a, dst, wc)] = (int8_t)e;
     uint16_t* prow = a.part + (size_t)dst * a.d + wc;
-    auto h16 = [&](float v) { return (uint32_t)f32_to_f16(__builtin_amdgcn_ldexpf(v, -e)); };
+    auto h16 = [&](float v0, float v1) {
+        return pack_f16x2(__builtin_amdgcn_ldexpf(v0, -e), __builtin_amdgcn_ldexpf(v1, -e));
+    };
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
         uint2 own_lo, own_hi;
-        own_lo.x = h16(acc[8 * m]) | (h16(acc[8 * m + 1]) << 16);
-        own_lo.y = h16(acc[8 * m + 2]) | (h16(acc[8 * m + 3]) << 16);
-        own_hi.x = h16(acc[8 * m + 4]) | (h16(acc[8 * m + 5]) << 16);
-        own_hi.y = h16(acc[8 * m + 6]) | (h16(acc[8 * m + 7]) << 16);
+        own_lo.x = h16(acc[8 * m], acc[8 * m + 1]);
+        own_lo.y = h16(acc[8 * m + 2], acc[8 * m + 3]);
+        own_hi.x = h16(acc[8 * m + 4], acc[8 * m + 5]);
+        own_hi.y = h16(acc[8 * m + 6], acc[8 * m + 7]);
         const uint2 send = half ? own_lo : own_hi;
         uint2 recv;
         recv.x = (uint32_t)__shfl_xor((int)send.x, 32, 64);
@@ -767,14 +769,14 @@ __global__ __launch_bounds__(kThreads) void down_resident_kernel(const PrefillAr
                 const int e = part_exp(pair_absmax(acc[ms]));
                 const int row_e = 32 * ms + t;
                 if (half == 0 && row_e < it.M) a.pexp[part_exp_index(a, s_dst[row_e], wc)] = (int8_t)e;
-                auto h16 = [&](float v) {
-                    return (uint32_t)f32_to_f16(__builtin_amdgcn_ldexpf(v, -e));
+                auto h16 = [&](float v0, float v1) {
+                    return pack_f16x2(__builtin_amdgcn_ldexpf(v0, -e), __builtin_amdgcn_ldexpf(v1, -e));
                 };
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {  // columns 8gq + 4h .. +3: 8-byte unit 2gq + h
                     uint2 v;
-                    v.x = h16(acc[ms][4 * gq]) | (h16(acc[ms][4 * gq + 1]) << 16);
-                    v.y = h16(acc[ms][4 * gq + 2]) | (h16(acc[ms][4 * gq + 3]) << 16);
+                    v.x = h16(acc[ms][4 * gq], acc[ms][4 * gq + 1]);
+                    v.y = h16(acc[ms][4 * gq + 2], acc[ms][4 * gq + 3]);
                     const int slot = gq ^ ((t >> 1) & 3);
                     *(uint2*)(so + t * 64 + 16 * slot + 8 * half) = v;
                 }

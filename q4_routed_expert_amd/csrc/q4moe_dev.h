@@ -48,8 +48,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
-__device__ __forceinline__ uint16_t f32_to_f16(float f) {
-    return __builtin_bit_cast(uint16_t, (_Float16)f);
+// Two floats as two round-to-nearest-even fp16 values in one word (low half =
+// lo): one v_cvt_pk_f16_f32 on gfx950, the same bits as two scalar casts.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    const float __attribute__((ext_vector_type(2))) v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
 }
 
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
