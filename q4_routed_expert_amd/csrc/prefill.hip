@@ -381,44 +381,39 @@ __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const Pre
     const int c0 = cb * kDnCols;
 
     // ---- 1. routed sums: thread (token row tr0 + 16 p, columns c0 + 8 c8 ..) ----
+    // The scores first (their LDS store then waits for them alone), then the
+    // staged rows of the first token rows, whose round trip runs under the
+    // shared expert's GEMM (phase 2); all rows are summed after it.
+    float wv[(kShMaxRows * kMaxTopK + kThreads - 1) / kThreads];
+#pragma unroll
+    for (int u = 0; u < (kRows * kMaxTopK + kThreads - 1) / kThreads; ++u) {
+        const int i = tid + kThreads * u;
+        const int ic = i < kRows * k && row0 + i / k < T ? i : 0;  // clamped, always valid
+        wv[u] = a.topk_w[(size_t)row0 * k + ic];
+    }
     const int c8 = tid & 31, tr0 = tid >> 5;
     const int col = c0 + 8 * c8;
     const bool col_ok = col < d;  // d is a multiple of 64: 8-column pieces are whole
     const int colc = col_ok ? col : c0;
+    // token rows p < kPre are loaded before the GEMM, the rest after it (two
+    // rows' 64 registers held across the GEMM made it spill; one row: none)
+    constexpr int kPre = kP < 2 ? kP : 1;
     u32x4 pv[kP][kMaxTopK];
     uint2 ev[kP];
-#pragma unroll
-    for (int p = 0; p < kP; ++p) {
+    auto load_rows = [&](int p) {
         const int tr = tr0 + 16 * p;
         const size_t tok = (size_t)row0 + (tr < M ? tr : 0);  // clamped, always valid
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s)
             pv[p][s] = *(const u32x4*)(a.part + (tok * k + (s < k ? s : 0)) * d + colc);
         ev[p] = *(const uint2*)(a.pexp + part_exp_index(a, (int)tok * k, colc));
-    }
-    for (int i = tid; i < kRows * k; i += kThreads)
-        s_w[i] = row0 + i / k < T ? a.topk_w[(size_t)row0 * k + i] : 0.0f;
-    __syncthreads();
+    };
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-        const int tr = tr0 + 16 * p;
-        if (tr < M && col_ok) {
-            float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p < kPre; ++p) load_rows(p);
 #pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s) {
-                if (s < k) {
-                    const float w = s_w[tr * k + s];
-                    const int e = (int)(int8_t)(((s < 4 ? ev[p].x : ev[p].y) >> (8 * (s & 3))) & 0xFFu);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc8[2 * i] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] & 0xFFFFu), e);
-                        acc8[2 * i + 1] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] >> 16), e);
-                    }
-                }
-            }
-            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8)) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
-            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8 + 1)) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
-        }
+    for (int u = 0; u < (kRows * kMaxTopK + kThreads - 1) / kThreads; ++u) {
+        const int i = tid + kThreads * u;
+        if (i < kRows * k) s_w[i] = row0 + i / k < T ? wv[u] : 0.0f;
     }
 
     // ---- 2. the shared expert's down GEMM of the block ----
@@ -443,6 +438,33 @@ __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const Pre
     } else {
         chunk_gemm<kRows, 1>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
     }
+
+    // ---- 1, continued: the routed sums into LDS (s_w is published by the
+    // GEMM's barriers) ----
+#pragma unroll
+    for (int p = kPre; p < kP; ++p) load_rows(p);
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+        const int tr = tr0 + 16 * p;
+        if (tr < M && col_ok) {
+            float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < kMaxTopK; ++s) {
+                if (s < k) {
+                    const float w = s_w[tr * k + s];
+                    const int e = (int)(int8_t)(((s < 4 ? ev[p].x : ev[p].y) >> (8 * (s & 3))) & 0xFFu);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc8[2 * i] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] & 0xFFFFu), e);
+                        acc8[2 * i + 1] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] >> 16), e);
+                    }
+                }
+            }
+            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8)) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
+            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8 + 1)) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
+        }
+    }
+
     __syncthreads();  // every wave is done with the activation tiles (the y tile reuses them)
 
     // ---- 3. y = bf16(routed sum + shared output) ----
