@@ -506,6 +506,8 @@ __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const Pre
 // ---------------------------------------------------------------------------
 // routed 128-row work items at most (the capacity of the 128-row work map)
 constexpr int kMaxRoutedItems = MOE_MAX_TOKENS * kMaxTopK / kMT + kMaxExperts;
+static_assert((unsigned long long)kMaxRoutedItems * (MOE_MAX_D / 256) * 6 * 2 * 1024 < (1ull << 32),
+              "32-bit run starts");
 
 __device__ __forceinline__ int unit_cost(int M) { return 2 + ((M + 31) >> 5); }
 
@@ -549,12 +551,14 @@ __device__ __forceinline__ void cost_prefix(int n_items, int n_cb, int* s_pre, i
 // First unit (item * n_cb + block) of run g of G; n_items * n_cb for g >= G.
 __device__ __forceinline__ int run_start(int g, int G, int n_items, int n_cb, const int* s_pre) {
     if (g >= G) return n_items * n_cb;
-    const long long C2 = 2ll * __builtin_amdgcn_readfirstlane(s_pre[n_items]);
+    // 32-bit arithmetic: 2 x the total cost times G stays below 2^32 (at most
+    // kMaxRoutedItems items x 32 column blocks x cost 6 x 2 x 1024 groups)
+    const uint32_t C2 = 2u * (uint32_t)__builtin_amdgcn_readfirstlane(s_pre[n_items]);
     auto owner = [&](int i, int b) {
         const int p0 = __builtin_amdgcn_readfirstlane(s_pre[i]);
         const int p1 = __builtin_amdgcn_readfirstlane(s_pre[i + 1]);
-        const long long mid = 2ll * p0 + (long long)(2 * b + 1) * ((p1 - p0) / n_cb);
-        return (int)(mid * G / C2);
+        const uint32_t mid = 2u * (uint32_t)p0 + (uint32_t)(2 * b + 1) * (uint32_t)((p1 - p0) / n_cb);
+        return (int)(mid * (uint32_t)G / C2);
     };
     int lo = 0, hi = n_items;
     while (lo < hi) {
@@ -931,6 +935,7 @@ constexpr int kGuPer = (kGuMaxItems + kGuThreads - 1) / kGuThreads;
 // estimated cost of a gate/up unit with `ms` 32-row subtiles
 __device__ __forceinline__ int gu_unit_cost(int ms) { return 2 + ms; }
 constexpr int kGuRunMax = 512;  // items one group may hold (s_items)
+static_assert((unsigned long long)kGuPer * 512 * 6 * 2 * 1024 < (1ull << 32), "32-bit run cut");
 
 // Routed item i of the gate/up kernel: part i % S of 128-row tile i / S of the
 // tile map (S = 1 << item_sh parts of 128 >> item_sh rows each).  Its rows end
@@ -1028,7 +1033,9 @@ __device__ __forceinline__ int item_run(const PrefillArgs& a, int n_raw, int n_t
         np += N[c];
         cp += N[c] * gu_unit_cost(c + 1);
     }
-    const long long den = 2LL * max(cp, 1);
+    // 32-bit arithmetic: (2 x cost prefix + cost) x Q stays below 2^32 (at
+    // most kGuPer x kGuThreads items of cost 6, Q <= 1024 groups)
+    const uint32_t den = 2u * (uint32_t)max(cp, 1);
     int before = 0, mine = 0;
     int pos[kGuPer];
 #pragma unroll
@@ -1040,7 +1047,7 @@ __device__ __forceinline__ int item_run(const PrefillArgs& a, int n_raw, int n_t
             const int cost = gu_unit_cost(c + 1);
             const int pre = (c == 0 ? cost0[0] : c == 1 ? cost0[1] : c == 2 ? cost0[2] : cost0[3]) +
                             k * cost;
-            const int run = (int)((long long)(2 * pre + cost) * Q / den);
+            const int run = (int)((uint32_t)(2 * pre + cost) * (uint32_t)Q / den);
             before += run < q;
             if (run == q) {
                 ++mine;
@@ -1499,7 +1506,7 @@ static int device_cus() {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cus[dev] = n;
+        cus[dev] = n < 1024 ? n : 1024;  // the schedules' 32-bit run cuts assume <= 1024 groups
     }
     return cus[dev];
 }
