@@ -207,10 +207,12 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
 
 // ---------------------------------------------------------------------------
 // Top-k of one token's logits by one wave (E <= 256: lane l holds experts
-// l, l + 64, l + 128, l + 192).  Selection compares fp32 logits: larger
-// first, equal logits -> lower expert index.  Each of the k rounds takes the
-// wave maximum of the order keys, then the wave minimum of the expert indices
-// holding it, and retires that key (all on the vector ALUs).
+// 4l .. 4l + 3, so lane order is expert order).  Selection compares fp32
+// logits: larger first, equal logits -> lower expert index.  Each of the k
+// rounds takes every lane's largest remaining key, the wave maximum of those
+// (one reduction on the vector ALUs), and the lowest lane holding it (a
+// ballot): that lane's lowest expert with the maximum key is the round's
+// pick, and the lane retires it.
 // Scores: softmax over the experts renormalised over the k selected ones,
 // computed as exp(l_s - l_max) / sum_s' exp(l_s' - l_max) with the sum taken
 // in slot order (the full-softmax normaliser cancels).  Lane s < k returns
@@ -221,11 +223,10 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E,
     uint32_t key[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
+        const int e = 4 * lane + i;
         key[i] = e < E ? logit_key(lrow[e]) : 0u;  // key 0: no finite logit, never chosen
     }
     auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
-    auto umin = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
     float sel_l[kMaxTopK];
     int my_e = 0;
     float my_l = 0.0f;
@@ -233,16 +234,19 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lrow, int E,
     for (int s = 0; s < kMaxTopK; ++s) {
         sel_l[s] = 0.0f;
         if (s < k) {
-            const uint32_t m = wave_reduce_u32(umax(umax(key[0], key[1]), umax(key[2], key[3])), umax);
-            uint32_t c = 0xFFFFu;
+            const uint32_t h = umax(umax(key[0], key[1]), umax(key[2], key[3]));
+            const uint32_t m = wave_reduce_u32(h, umax);
+            // the lowest lane whose largest key is m holds the lowest expert with key m
+            const int win = (int)__builtin_ctzll(__ballot(h == m));
+            const int i_lo = key[0] == m ? 0 : key[1] == m ? 1 : key[2] == m ? 2 : 3;
+            const int e = 4 * win + __builtin_amdgcn_readlane(i_lo, win);
+            if (lane == win) {
 #pragma unroll
-            for (int i = 3; i >= 0; --i) c = key[i] == m ? (uint32_t)(64 * i + lane) : c;
-            const uint32_t e = wave_reduce_u32(c, umin);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) key[i] = (uint32_t)(64 * i + lane) == e ? 0u : key[i];
+                for (int i = 0; i < 4; ++i) key[i] = i == i_lo ? 0u : key[i];
+            }
             sel_l[s] = key_logit(m);
             if (s == lane) {
-                my_e = (int)e;
+                my_e = e;
                 my_l = sel_l[s];
             }
         }
