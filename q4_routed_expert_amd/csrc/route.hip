@@ -126,6 +126,155 @@ __global__ __launch_bounds__(64 * kRtWaves) void router_logits_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same logits for d a multiple of 1024 (the work group, wave and K split
+// as above; the same MFMA operands in the same order, so the same bits), with
+// the operands streamed differently: each wave stages its own 64 x rows
+// through LDS in chunks of 64 k (8 KB, two buffers per wave), loaded straight
+// into LDS 8 rows x 128 bytes per instruction (so a load instruction touches 8
+// rows instead of 32) with the 16-byte columns XOR-swizzled by row on the
+// source side; W_r comes as 32-bit buffer loads whose row steps are scalar
+// offsets, one chunk ahead; hi and lo are formed two values per conversion.
+// Rows past T and columns past E read clamped, valid data and are not stored.
+// ---------------------------------------------------------------------------
+constexpr int kRlChunk = 64;                 // k per staged chunk
+constexpr int kRlRowB = kRlChunk * 2;        // bytes per staged row
+constexpr int kRlBufB = kRtM * kRlRowB;      // 8 KB per chunk buffer
+
+__device__ __forceinline__ void split_hi_lo_pk(const float (&w)[8], bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        h[p] = pack_bf16x2(w[2 * p], w[2 * p + 1]);
+        const float h0 = __uint_as_float(h[p] << 16), h1 = __uint_as_float(h[p] & 0xFFFF0000u);
+        l[p] = pack_bf16x2(w[2 * p] - h0, w[2 * p + 1] - h1);
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// s_waitcnt vmcnt(N), the other counters not waited on
+template <int N>
+__device__ __forceinline__ void rl_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__global__ __launch_bounds__(64 * kRtWaves) void router_logits_lds_kernel(
+    const uint16_t* __restrict__ x, int T, int d, const float* __restrict__ W,
+    const float* __restrict__ bias, int E, float* __restrict__ logits,
+    int32_t* __restrict__ blk_counts, int n_counts) {
+    static_assert((kRtWaves - 1) * 2 * 16 * 64 * 4 <= kRtWaves * 2 * kRlBufB, "reduction fits the staging LDS");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kRtWaves * 2 * kRlBufB];  // 128 KB
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counts; i += gridDim.x * blockDim.x)
+        blk_counts[i] = 0;
+    const int n_eb = (E + kRtN - 1) / kRtN;
+    const int n_wg = gridDim.x, g = blockIdx.x, xcd = g & 7;
+    int base = 0;
+    for (int xx = 0; xx < xcd; ++xx) base += (n_wg - xx + 7) >> 3;
+    const int wi = base + (g >> 3);
+    const int t0 = (wi / n_eb) * kRtM, e0 = (wi - (wi / n_eb) * n_eb) * kRtN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+    const int n = e0 + (lane & 31);
+    const int kq = d / kRtWaves, kbeg = wave * kq;
+    const int n_chunks = kq / kRlChunk;  // even: d % 1024 == 0
+    unsigned char* buf = smem + wave * 2 * kRlBufB;
+    // direct-to-LDS source offsets: instruction i covers staged rows 8i .. 8i + 7,
+    // lane -> row 8i + lane / 8, LDS column lane % 8, source column (lane % 8) ^ (row % 8)
+    uint32_t xsrc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const uint32_t t = (uint32_t)(t0 + r < T ? t0 + r : T - 1);  // clamped, always valid
+        xsrc[i] = (t * (uint32_t)d + (uint32_t)kbeg) * 2u + (uint32_t)((((lane & 7) ^ (r & 7))) << 4);
+    }
+    const uint32_t w_b = ((uint32_t)(n < E ? n : E - 1) + (uint32_t)(kbeg + 8 * half) * (uint32_t)E) * 4u;
+    f32x16 acc0 = {}, acc1 = {};
+    float wv[2][4][8];
+    // generic lambdas: the buffer builtins stay out of the host pass
+    auto dma = [&](auto, int c, int b) {
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)x, 0, (int)((uint32_t)T * (uint32_t)d * 2u), 0x00020000);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void*)(buf + b * kRlBufB + i * 1024), 16, xsrc[i],
+                c * kRlRowB, 0, 0);
+    };
+    auto wload = [&](auto, int c, int b) {
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)W, 0, (int)((uint32_t)d * (uint32_t)E * 4u), 0x00020000);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                wv[b][st][i] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rw, w_b, (c * kRlChunk + 16 * st + i) * E * 4, 0));
+    };
+    dma(0, 0, 0);
+    wload(0, 0, 0);
+    for (int c0 = 0; c0 < n_chunks; c0 += 2) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int c = c0 + b;
+            __builtin_amdgcn_sched_barrier(0);
+            // chunk c has landed in LDS: of the loads issued since its direct-to-LDS
+            // loads only W's 32 of the same chunk may still be in flight (the
+            // compiler does not order these LDS reads after those loads itself)
+            rl_wait_vm<32>();
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 A[4][2];
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    const int r = 32 * f + (lane & 31), col = 2 * st + half;
+                    A[st][f] = *(const bf16x8*)(buf + b * kRlBufB + r * kRlRowB + ((col ^ (r & 7)) << 4));
+                }
+            // the next chunk into the other buffer (the last one repeats a chunk:
+            // the same 40 loads every time keep the counts above exact)
+            const int cn = c + 1 < n_chunks ? c + 1 : c;
+            dma(0, cn, b ^ 1);
+            wload(0, cn, b ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                bf16x8 hi, lo;
+                split_hi_lo_pk(wv[b][st], hi, lo);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st][0], hi, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st][1], hi, acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st][0], lo, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st][1], lo, acc1, 0, 0, 0);
+            }
+        }
+    }
+    rl_wait_vm<0>();  // the repeated last chunk has landed before the LDS is reused
+    __syncthreads();
+    float* red = (float*)smem;  // [kRtWaves - 1][2][16][64]
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            red[(((wave - 1) * 2 + 0) * 16 + i) * 64 + lane] = acc0[i];
+            red[(((wave - 1) * 2 + 1) * 16 + i) * 64 + lane] = acc1[i];
+        }
+    }
+    __syncthreads();
+    if (wave > 0 || n >= E) return;
+    const float bb = bias ? bias[n] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * half + (i & 3);
+        float v0 = acc0[i], v1 = acc1[i];
+#pragma unroll
+        for (int w = 0; w < kRtWaves - 1; ++w) {
+            v0 += red[((w * 2 + 0) * 16 + i) * 64 + lane];
+            v1 += red[((w * 2 + 1) * 16 + i) * 64 + lane];
+        }
+        if (t0 + r < T) logits[(size_t)(t0 + r) * E + n] = v0 + bb;
+        if (t0 + 32 + r < T) logits[(size_t)(t0 + 32 + r) * E + n] = v1 + bb;
+    }
+}
+
 __global__ __launch_bounds__(256) void zero_counts_kernel(int32_t* __restrict__ blk_counts,
                                                           int n_counts) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n_counts; i += gridDim.x * blockDim.x)
@@ -141,8 +290,12 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int d, const float* w_
                            blk_counts, n_counts);
     } else {
         const int grid = ((T + kRtM - 1) / kRtM) * ((E + kRtN - 1) / kRtN);
-        hipLaunchKernelGGL(router_logits_kernel, dim3(grid), dim3(64 * kRtWaves), 0, s, x, T, d,
-                           w_router, router_bias, E, logits, blk_counts, n_counts);
+        if (d % (kRtWaves * 2 * kRlChunk) == 0)
+            hipLaunchKernelGGL(router_logits_lds_kernel, dim3(grid), dim3(64 * kRtWaves), 0, s, x, T,
+                               d, w_router, router_bias, E, logits, blk_counts, n_counts);
+        else
+            hipLaunchKernelGGL(router_logits_kernel, dim3(grid), dim3(64 * kRtWaves), 0, s, x, T, d,
+                               w_router, router_bias, E, logits, blk_counts, n_counts);
     }
     trace_point(s);
     return hipGetLastError();

@@ -321,6 +321,8 @@ EDGE = [
                                           # load per unit, several items per expert, ragged tails
     (300, 512, 448, 16, 4, True, 12),     # inter = 448: the resident down GEMM, odd group count
     (257, 64, 512, 8, 3, False, 13),      # the smallest d (router with one K-step per wave)
+    (130, 2048, 128, 40, 3, True, 14),    # router staged through LDS: ragged token and
+                                          # expert tiles (rows and columns clamped)
 ]
 
 
