@@ -184,11 +184,17 @@ __device__ __forceinline__ void load_bchunk(const Q4& W, size_t wrow, int K, int
 // accumulates acc[ms] for the NMS active 32-row subtiles.  The tile has kRowsT
 // rows; src_row[p] is the activation row of tile row (tid + kThreads p) / 16
 // (-1: none, zeros).  Contains barriers: every thread of the work group calls
-// it with the same NMS.
-template <int kRowsT, int NMS>
+// it with the same NMS.  hook(u, c0) runs after the u-th chunk of every group
+// of kStages chunks starting at chunk c0 (u a fully unrolled index), so that
+// a caller can interleave its own loads and vector work with the GEMM.
+struct NoHook {
+    __device__ __forceinline__ void operator()(int, int) const {}
+};
+
+template <int kRowsT, int NMS, bool kOneGroup = false, class Hook = NoHook>
 __device__ __forceinline__ void chunk_gemm(const uint16_t* A, const int (&src_row)[kRowsT * kSlots / kThreads],
                                            int K, const Q4& W, size_t wrow, bool wave_on,
-                                           unsigned char* lds, f32x16 (&acc)[4]) {
+                                           unsigned char* lds, f32x16 (&acc)[4], Hook hook = Hook()) {
     constexpr int kAL = kRowsT * kSlots / kThreads;  // 16-byte activation loads per thread per chunk
     constexpr int kBuf = kRowsT * kRowBytes;
     static_assert(kRowsT * kSlots % kThreads == 0 && 32 * NMS <= kRowsT, "tile split");
@@ -264,7 +270,9 @@ __device__ __forceinline__ void chunk_gemm(const uint16_t* A, const int (&src_ro
     // Chunks c+1 .. c+kStages-1 are in flight while chunk c is consumed.  The
     // loop runs a multiple of kStages chunks; chunks past K load clamped
     // addresses (recently read lines) and contribute zeros.
-    const int n_loop = (n_chunks + kStages - 1) / kStages * kStages;
+    // kOneGroup: the caller guarantees K <= kStages * kKC (one group, a
+    // straight-line body)
+    const int n_loop = kOneGroup ? kStages : (n_chunks + kStages - 1) / kStages * kStages;
 #pragma unroll
     for (int u = 0; u < kStages - 1; ++u) {
         load_a(u, ast[u]);
@@ -280,6 +288,7 @@ __device__ __forceinline__ void chunk_gemm(const uint16_t* A, const int (&src_ro
             load_a(c + kStages - 1, ast[nx]);
             load_b(c + kStages - 1, bst[nx]);
             if (wave_on) compute(c, u & 1, bst[u]);
+            hook(u, c0);
         }
     }
 }
@@ -342,12 +351,12 @@ __global__ __launch_bounds__(kThreads) void down_chunked_kernel(const PrefillArg
 
 // ---------------------------------------------------------------------------
 // The shared expert's down projection with the combine.  Work item = a block of
-// kRows (32 or 64) tokens x 256 output columns.  Three phases:
-//   1. the k staged partial rows of every token of the block are read with
-//      contiguous 16-byte loads (32 threads cover one token's 256 columns, every
-//      load issued before any is used), unscaled, weighted by the scores and
-//      summed in slot order into an fp32 tile in LDS;
-//   2. the shared expert's down GEMM of the block (chunk_gemm);
+// kRows (32 or 64) tokens x 256 output columns.  Phases:
+//   1+2. the shared expert's down GEMM of the block (chunk_gemm), and between
+//      its chunks the k staged partial rows of one token row per thread (32
+//      threads cover one token's 256 columns with contiguous 16-byte loads,
+//      issued a chunk ahead) weighted by the scores times their staging
+//      exponents and summed in slot order into an fp32 tile in LDS;
 //   3. y = bf16(routed sum + shared output), staged through LDS so that the
 //      global stores are contiguous 16-byte pieces.
 // ---------------------------------------------------------------------------
@@ -359,7 +368,7 @@ __device__ __forceinline__ int rsum_off(int r, int g) { return r * 1024 + ((g ^ 
 // 16-byte granule g of row r of the bf16 output tile (512-byte rows).
 __device__ __forceinline__ int ytile_off(int r, int g) { return r * 512 + ((g ^ (r & 31)) << 4); }
 
-template <int kRows>
+template <int kRows, bool kInterleave>
 __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const PrefillArgs a,
                                                                        const int n_items,
                                                                        const int n_cb,
@@ -369,7 +378,6 @@ __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const Pre
     constexpr int kAL = kRows * kSlots / kThreads;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kShMaxRows * kRowBytes];
     __shared__ __attribute__((aligned(16))) unsigned char s_rsum[kShMaxRows * 1024];
-    __shared__ float s_w[kShMaxRows * kMaxTopK];
 
     const int b = blockIdx.x;
     const int L = (b & 7) * (n_wg >> 3) + (b >> 3);
@@ -381,42 +389,54 @@ __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const Pre
     const int c0 = cb * kDnCols;
 
     // ---- 1. routed sums: thread (token row tr0 + 16 p, columns c0 + 8 c8 ..) ----
-    // The scores first (their LDS store then waits for them alone), then the
-    // staged rows of the first token rows, whose round trip runs under the
-    // shared expert's GEMM (phase 2); all rows are summed after it.
-    float wv[(kShMaxRows * kMaxTopK + kThreads - 1) / kThreads];
-#pragma unroll
-    for (int u = 0; u < (kRows * kMaxTopK + kThreads - 1) / kThreads; ++u) {
-        const int i = tid + kThreads * u;
-        const int ic = i < kRows * k && row0 + i / k < T ? i : 0;  // clamped, always valid
-        wv[u] = a.topk_w[(size_t)row0 * k + ic];
-    }
+    // kInterleave (inter <= kStages chunks, so the GEMM runs one group of
+    // kStages chunks): row p's staged partials, staging exponents and scores
+    // are loaded one GEMM chunk ahead and summed after the GEMM's chunk p (the
+    // hook below), so that their round trips and vector work run under the
+    // shared expert's GEMM; otherwise every row after the GEMM.  Each score is
+    // scaled by its slot's staging exponent once (an exact power-of-two
+    // scaling), and the fp16 values then enter the fma directly.
     const int c8 = tid & 31, tr0 = tid >> 5;
     const int col = c0 + 8 * c8;
     const bool col_ok = col < d;  // d is a multiple of 64: 8-column pieces are whole
     const int colc = col_ok ? col : c0;
-    // token rows p < kPre are loaded before the GEMM, the rest after it (two
-    // rows' 64 registers held across the GEMM made it spill; one row: none)
-    constexpr int kPre = kP < 2 ? kP : 1;
+    static_assert(kP <= kStages, "one token row per GEMM chunk");
     u32x4 pv[kP][kMaxTopK];
     uint2 ev[kP];
+    float sw[kP][kMaxTopK];
     auto load_rows = [&](int p) {
         const int tr = tr0 + 16 * p;
         const size_t tok = (size_t)row0 + (tr < M ? tr : 0);  // clamped, always valid
 #pragma unroll
-        for (int s = 0; s < kMaxTopK; ++s)
+        for (int s = 0; s < kMaxTopK; ++s) {
             pv[p][s] = *(const u32x4*)(a.part + (tok * k + (s < k ? s : 0)) * d + colc);
+            sw[p][s] = a.topk_w[tok * k + (s < k ? s : 0)];
+        }
         ev[p] = *(const uint2*)(a.pexp + part_exp_index(a, (int)tok * k, colc));
     };
+    auto sum_rows = [&](int p) {
+        const int tr = tr0 + 16 * p;
+        if (tr < M && col_ok) {
+            float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int p = 0; p < kPre; ++p) load_rows(p);
+            for (int s = 0; s < kMaxTopK; ++s) {
+                if (s < k) {
+                    const int e = (int)(int8_t)(((s < 4 ? ev[p].x : ev[p].y) >> (8 * (s & 3))) & 0xFFu);
+                    const float w = __builtin_amdgcn_ldexpf(sw[p][s], e);
 #pragma unroll
-    for (int u = 0; u < (kRows * kMaxTopK + kThreads - 1) / kThreads; ++u) {
-        const int i = tid + kThreads * u;
-        if (i < kRows * k) s_w[i] = row0 + i / k < T ? wv[u] : 0.0f;
-    }
+                    for (int i = 0; i < 4; ++i) {
+                        acc8[2 * i] = __builtin_fmaf(f16_to_f32(pv[p][s][i] & 0xFFFFu), w, acc8[2 * i]);
+                        acc8[2 * i + 1] = __builtin_fmaf(f16_to_f32(pv[p][s][i] >> 16), w, acc8[2 * i + 1]);
+                    }
+                }
+            }
+            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8)) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
+            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8 + 1)) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
+        }
+    };
+    if constexpr (kInterleave) load_rows(0);
 
-    // ---- 2. the shared expert's down GEMM of the block ----
+    // ---- 2. the shared expert's down GEMM of the block, with the routed sums ----
     const int wcol0 = c0 + 32 * wave;
     const bool wave_on = wcol0 < d;
     const size_t wrow = wave_on ? (size_t)(wcol0 + (lane & 31)) : 0;
@@ -430,39 +450,29 @@ __global__ __launch_bounds__(kThreads) void shared_down_combine_kernel(const Pre
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
     const int n_ms = (M + 31) >> 5;
+    // with kInterleave the GEMM runs exactly one group of kStages chunks, so the
+    // hook sees u = 0 .. kStages - 1 once: token row u is summed after chunk u
+    auto hook = [&](int u, int) {
+        if constexpr (kInterleave) {
+            if (u < kP) {
+                if (u + 1 < kP) load_rows(u + 1);
+                sum_rows(u);
+            }
+        }
+    };
     if constexpr (kRows == 64) {
         if (n_ms == 2)
-            chunk_gemm<kRows, 2>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
+            chunk_gemm<kRows, 2, kInterleave>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc, hook);
         else
-            chunk_gemm<kRows, 1>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
+            chunk_gemm<kRows, 1, kInterleave>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc, hook);
     } else {
-        chunk_gemm<kRows, 1>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc);
+        chunk_gemm<kRows, 1, kInterleave>(a.h_sh, src_row, a.I, a.sh_down, wrow, wave_on, lds, acc, hook);
     }
-
-    // ---- 1, continued: the routed sums into LDS (s_w is published by the
-    // GEMM's barriers) ----
+    if constexpr (!kInterleave) {
 #pragma unroll
-    for (int p = kPre; p < kP; ++p) load_rows(p);
+        for (int p = 0; p < kP; ++p) load_rows(p);
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
-        const int tr = tr0 + 16 * p;
-        if (tr < M && col_ok) {
-            float acc8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < kMaxTopK; ++s) {
-                if (s < k) {
-                    const float w = s_w[tr * k + s];
-                    const int e = (int)(int8_t)(((s < 4 ? ev[p].x : ev[p].y) >> (8 * (s & 3))) & 0xFFu);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc8[2 * i] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] & 0xFFFFu), e);
-                        acc8[2 * i + 1] += w * __builtin_amdgcn_ldexpf(f16_to_f32(pv[p][s][i] >> 16), e);
-                    }
-                }
-            }
-            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8)) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
-            *(f32x4*)(s_rsum + rsum_off(tr, 2 * c8 + 1)) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
-        }
+        for (int p = 0; p < kP; ++p) sum_rows(p);
     }
 
     __syncthreads();  // every wave is done with the activation tiles (the y tile reuses them)
@@ -1569,12 +1579,19 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     const int rows = shared_down_rows(a.T, n_cb);
     const int n_items = (a.T + rows - 1) / rows;
     const int n_wg = ((n_items * n_cb) + 7) & ~7;
-    if (rows == 64)
-        hipLaunchKernelGGL(shared_down_combine_kernel<64>, dim3(n_wg), dim3(kThreads), 0, s, a,
-                           n_items, n_cb, n_wg);
+    const bool il = a.I <= kStages * kKC;  // the shared GEMM is one group of chunks
+    if (rows == 64 && il)
+        hipLaunchKernelGGL((shared_down_combine_kernel<64, true>), dim3(n_wg), dim3(kThreads), 0, s,
+                           a, n_items, n_cb, n_wg);
+    else if (rows == 64)
+        hipLaunchKernelGGL((shared_down_combine_kernel<64, false>), dim3(n_wg), dim3(kThreads), 0, s,
+                           a, n_items, n_cb, n_wg);
+    else if (il)
+        hipLaunchKernelGGL((shared_down_combine_kernel<32, true>), dim3(n_wg), dim3(kThreads), 0, s,
+                           a, n_items, n_cb, n_wg);
     else
-        hipLaunchKernelGGL(shared_down_combine_kernel<32>, dim3(n_wg), dim3(kThreads), 0, s, a,
-                           n_items, n_cb, n_wg);
+        hipLaunchKernelGGL((shared_down_combine_kernel<32, false>), dim3(n_wg), dim3(kThreads), 0, s,
+                           a, n_items, n_cb, n_wg);
     trace_point(s);
     return hipGetLastError();
 }
