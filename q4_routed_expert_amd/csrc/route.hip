@@ -212,6 +212,7 @@ __global__ __launch_bounds__(64 * kRtWaves) void router_logits_lds_kernel(
                     float, __builtin_amdgcn_raw_buffer_load_b32(rw, w_b, (c * kRlChunk + 16 * st + i) * E * 4, 0));
     };
     dma(0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     wload(0, 0, 0);
     for (int c0 = 0; c0 < n_chunks; c0 += 2) {
 #pragma unroll
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(64 * kRtWaves) void router_logits_lds_kernel(
             // the same 40 loads every time keep the counts above exact)
             const int cn = c + 1 < n_chunks ? c + 1 : c;
             dma(0, cn, b ^ 1);
+            __builtin_amdgcn_sched_barrier(0);  // the count above needs the LDS loads issued first
             wload(0, cn, b ^ 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
