@@ -162,6 +162,9 @@ def roofline(flops, nbytes, seconds):
             "frac": round(a / PEAK_HBM_GBPS, 4), "traffic": None}
 
 
+GRAPH_LAYERS = 8  # prefill layer steps per HIP-graph replay
+
+
 def bench_prefill(args, q4, torch, ev, stream):
     from workloads import WORKLOADS, make_layer
     w = WORKLOADS["prefill2048"]
@@ -240,22 +243,24 @@ def bench_prefill(args, q4, torch, ev, stream):
         "gbps": work["bytes"] / sec / 1e9, "work": work, "kernel_us": {n: v * 1e3 for n, v in per.items()},
         "clocks_under_load": under_load,
     }
-    # two layer steps (route + prefill on each weight set) captured once in a
-    # HIP graph and replayed; the output must equal the eager output
+    # GRAPH_LAYERS layer steps (route + prefill, alternating the weight sets)
+    # captured once in a HIP graph and replayed; the output must equal the
+    # eager output.  A replay carries a fixed cost of its own (about 30 us
+    # here), so a replay holds several layers, as a model's forward would.
     if not args.no_graph:
-        for i in range(2):
+        for i in range(GRAPH_LAYERS):
             step(i)
         torch.cuda.synchronize()
         y_eager = y.clone()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(2):
+            for i in range(GRAPH_LAYERS):
                 step(i)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         same = bool(torch.equal(y, y_eager))
-        reps = max(1, K // 2)
+        reps = max(1, K // GRAPH_LAYERS)
         t2 = ev.make(2)
         gs = int(torch.cuda.current_stream().cuda_stream)
         ev.record(t2[0], gs)
@@ -263,10 +268,10 @@ def bench_prefill(args, q4, torch, ev, stream):
             g.replay()
         ev.record(t2[1], gs)
         torch.cuda.synchronize()
-        us_g = ev.ms(t2[0], t2[1]) * 1e3 / (2 * reps)
+        us_g = ev.ms(t2[0], t2[1]) * 1e3 / (GRAPH_LAYERS * reps)
         out["graph"] = {"us_per_layer": us_g, "tok_s": w.T / (us_g * 1e-6),
                         "mfma_frac": work["flops"] / (us_g * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                        "replays": reps, "layers_per_replay": 2, "matches_eager": same}
+                        "replays": reps, "layers_per_replay": GRAPH_LAYERS, "matches_eager": same}
         log(f"prefill graph: {us_g:.1f} us/layer, output equal to eager: {same}")
         del g
     gu_sec = per["gate_up"] / 1e3
