@@ -103,7 +103,7 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Workspace: [decode region | prefill region], so one workspace sized for T
 // tokens serves both entry points.
 struct DecodeWs {
-    size_t sel_idx, sel_w, logits, partial, h, total;
+    size_t sel_idx, sel_w, logits, partial, h, y_sh, total;
 };
 DecodeWs decode_ws(const moe_layer* L) {
     DecodeWs w;
@@ -116,6 +116,7 @@ DecodeWs decode_ws(const moe_layer* L) {
     o += align256(sizeof(float) * (size_t)((L->d + MOE_DECODE_ROUTER_ROWS - 1) / MOE_DECODE_ROUTER_ROWS) *
                   nt * L->n_experts);
     w.h = o; o += align256(sizeof(uint16_t) * nt * (size_t)(L->top_k + 1) * L->inter);
+    w.y_sh = o; o += align256(sizeof(float) * nt * (size_t)L->d);
     w.total = o;
     return w;
 }
@@ -315,6 +316,7 @@ int decode_launch(const moe_layer* L, const uint16_t* x, int32_t T, uint32_t fla
     a.sel_idx = (int32_t*)(base + dw.sel_idx);
     a.sel_w = (float*)(base + dw.sel_w);
     a.h = (uint16_t*)(base + dw.h);
+    a.y_sh = (float*)(base + dw.y_sh);
     a.y = y;
     trace_begin((hipStream_t)stream);
     return hip_status(q4moe::launch_decode(a, (hipStream_t)stream), "decode");

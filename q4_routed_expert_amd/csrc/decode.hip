@@ -17,12 +17,15 @@
 //      expert's gate/up rows, which need no routing;
 //   2. every work group adds the partial sums in a fixed order (+ bias) and
 //      runs the top-k itself -- the same arithmetic in every work group, so
-//      every one finds the same experts -- then computes gate/up rows of its
-//      routed slot: one wave per (slot, intermediate row j), the gate and up
-//      rows streamed once with 16-byte loads per lane, h = bf16(SiLU(g) * u);
-//   3. down: 16 lanes per (output row, expert) task, 16-byte pieces per lane;
-//      the selected experts, h and every weight piece are loaded before any
-//      arithmetic, and y = bf16( sum_s w_s * P_s (slot order) + P_shared ).
+//      every one finds the same experts -- while its other waves compute rows
+//      of the shared expert's down projection (its h is ready, and it needs
+//      no routing); then it computes gate/up rows of its routed slot: one
+//      wave per (slot, intermediate row j), the gate and up rows streamed
+//      once with 16-byte loads per lane, h = bf16(SiLU(g) * u);
+//   3. down: 16 lanes per (output row, routed expert) task, 16-byte pieces
+//      per lane; the selected experts, h and every weight piece are loaded
+//      before any arithmetic, and y = bf16( sum_s w_s * P_s (slot order) +
+//      P_shared ).
 // Every weight enters as the bf16 value bf16(q * s + b), the same operand the
 // grouped GEMM feeds its matrix cores, so prefill and decode compute one
 // function of the layer.
@@ -339,6 +342,50 @@ __global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeA
         s_logits[tid] = v;
     }
     __syncthreads();
+    if (wave > 0) {
+        // rows n of the shared expert's down projection for every token (the
+        // work groups split the d rows evenly; waves 1..15 take rows in turn):
+        // a lane dequantises one code word per 512-wide pass once and dots it
+        // with each token's h, then a fixed DPP sum over the wave
+        const int n_wg = (int)(gridDim.x * gridDim.y), g = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+        const int per = (a.d + n_wg - 1) / n_wg, n_beg = g * per;
+        const int n_end = min(a.d, n_beg + per), I = a.I, T = a.T;
+        for (int n = n_beg + wave - 1; n < n_end; n += 15) {
+            float acc[MOE_MAX_DECODE_TOKENS];
+#pragma unroll
+            for (int tt = 0; tt < MOE_MAX_DECODE_TOKENS; ++tt) acc[tt] = 0.0f;
+            for (int kb = 0; kb < I; kb += 512) {
+                const int k0 = kb + 8 * lane;
+                const int kk = k0 < I ? k0 : 0;  // clamped, always valid; masked below
+                const uint32_t w = a.sh_down.q[(size_t)n * (I / 8) + kk / 8];
+                const size_t gi = (size_t)n * (I / kGroup) + kk / kGroup;
+                const bf16x8 wv = dequant8(w, dq_scale(a.sh_down.scale[gi]), bf16_to_f32(a.sh_down.bias[gi]));
+#pragma unroll
+                for (int tt = 0; tt < MOE_MAX_DECODE_TOKENS; ++tt) {
+                    if (tt < T) {  // uniform
+                        const u32x4 hv = *(const u32x4*)(a.h + ((size_t)(tt * (k + 1) + k) * I + kk));
+                        const bf16x8 xv = __builtin_bit_cast(bf16x8, hv);
+                        float p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 0, 1),
+                                                                  __builtin_shufflevector(xv, xv, 0, 1), 0.0f, false);
+                        p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 2, 3),
+                                                            __builtin_shufflevector(xv, xv, 2, 3), p, false);
+                        p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 4, 5),
+                                                            __builtin_shufflevector(xv, xv, 4, 5), p, false);
+                        p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 6, 7),
+                                                            __builtin_shufflevector(xv, xv, 6, 7), p, false);
+                        acc[tt] += k0 < I ? p : 0.0f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int tt = 0; tt < MOE_MAX_DECODE_TOKENS; ++tt) {
+                if (tt < T) {
+                    const float v = wave_sum_dpp(acc[tt]);
+                    if (lane == 0) a.y_sh[(size_t)tt * a.d + n] = v;
+                }
+            }
+        }
+    }
     if (wave == 0) {
         int se;
         float sw;
@@ -364,20 +411,20 @@ __global__ __launch_bounds__(1024) void decode_topk_gate_up_kernel(const DecodeA
 }
 
 // Down + combine for one token t = blockIdx.y and output rows n0 .. n0 + 7
-// (n0 = 8 blockIdx.x): the row tasks (output row, slot) -- slots 0..k-1 the
-// routed experts, slot k the shared expert -- go to 32 groups of 16 lanes
-// (task rt = group + 32 m); lane l of a group takes the 16-byte pieces
-// l, l + 16, .. (32 intermediate values each) of its task's weight row, so a
-// load instruction reads 64 contiguous bytes of each of four rows.  The
-// selected experts are loaded first, then the token's h (staged in LDS), then
-// every weight piece of the lane, all before any arithmetic.  Per task: the
-// lane's pieces in order, then a fixed DPP sum over the 16 lanes; the combine
-// adds w_s * P_s in slot order and the shared expert last.
-//   NM: tasks per lane group, ceil(8 (k + 1) / 32);  JP: pieces per lane per
-//   task, ceil(inter / 512).
+// (n0 = 8 blockIdx.x): the row tasks (output row, routed slot s < k) go to 32
+// groups of 16 lanes (task rt = group + 32 m); lane l of a group takes the
+// 16-byte pieces l, l + 16, .. (32 intermediate values each) of its task's
+// weight row, so a load instruction reads 64 contiguous bytes of each of four
+// rows.  The selected experts are loaded first, then the token's routed h
+// (staged in LDS), then every weight piece of the lane, all before any
+// arithmetic.  Per task: the lane's pieces in order, then a fixed DPP sum
+// over the 16 lanes; the combine adds w_s * P_s in slot order and the shared
+// expert's output (computed by the top-k kernel) last.
+//   NM: tasks per lane group, ceil(8 k / 32);  JP: pieces per lane per task,
+//   ceil(inter / 512).
 constexpr int kDnOutRows = 8;
 constexpr int kDnThreads = 512;
-constexpr int kDnStage = ((kMaxTopK + 1) * MOE_MAX_INTER / 8 + kDnThreads - 1) / kDnThreads;
+constexpr int kDnStage = (kMaxTopK * MOE_MAX_INTER / 8 + kDnThreads - 1) / kDnThreads;
 
 // Sum over each row of 16 lanes, left in every lane of the row (fixed order).
 __device__ __forceinline__ float row16_sum(float v) {
@@ -390,26 +437,29 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 template <int NM, int JP>
 __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(const DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_h[(kMaxTopK + 1) * MOE_MAX_INTER];
-    __shared__ float s_res[kDnOutRows * (kMaxTopK + 1)];
+    __shared__ __attribute__((aligned(16))) uint16_t s_h[kMaxTopK * MOE_MAX_INTER];
+    __shared__ float s_res[kDnOutRows * kMaxTopK];
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const int I = a.I, k = a.k, d = a.d, t = blockIdx.y, n0 = blockIdx.x * kDnOutRows;
-    const int K1 = k + 1, n_rt = kDnOutRows * K1, P = I / 32;
+    const int n_rt = kDnOutRows * k, P = I / 32;
     // 1. the experts of this lane's tasks
     int ex[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
         const int rt = grp + 32 * m;
-        const int s = rt < n_rt ? rt % K1 : 0;
-        ex[m] = a.sel_idx[(size_t)t * k + (s < k ? s : 0)];
+        const int s = rt < n_rt ? rt % k : 0;
+        ex[m] = a.sel_idx[(size_t)t * k + s];
     }
+    // the shared expert's output for the combine (threads 0..7, one row each)
+    const float ysh = a.y_sh[(size_t)t * d + n0 + (tid < kDnOutRows ? tid : 0)];
     // the combine's scores (threads 0..7, one output row each)
     float wsc[kMaxTopK];
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) wsc[s] = a.sel_w[(size_t)t * k + (s < k ? s : 0)];
-    // 2. the token's h: (k + 1) x inter bf16, every load in flight at once
-    const int n_h = K1 * I / 8;
-    const u32x4* h_src = (const u32x4*)(a.h + (size_t)t * K1 * I);
+    // 2. the token's routed h: k x inter bf16 (the first k of its k + 1 rows),
+    // every load in flight at once
+    const int n_h = k * I / 8;
+    const u32x4* h_src = (const u32x4*)(a.h + (size_t)t * (k + 1) * I);
     u32x4 hv[kDnStage];
 #pragma unroll
     for (int u = 0; u < kDnStage; ++u) {
@@ -423,12 +473,11 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(const DecodeArg
     for (int m = 0; m < NM; ++m) {
         const int rt = grp + 32 * m;
         const int rtc = rt < n_rt ? rt : 0;
-        const int nl = rtc / K1, s = rtc - nl * K1;
-        const bool sh = s == k;
-        const uint32_t* Wq = sh ? a.sh_down.q : a.down.q;
-        const uint16_t* Ws = sh ? a.sh_down.scale : a.down.scale;
-        const uint16_t* Wb = sh ? a.sh_down.bias : a.down.bias;
-        const size_t row = (sh ? 0 : (size_t)ex[m] * d) + n0 + nl;
+        const int nl = rtc / k;
+        const uint32_t* Wq = a.down.q;
+        const uint16_t* Ws = a.down.scale;
+        const uint16_t* Wb = a.down.bias;
+        const size_t row = (size_t)ex[m] * d + n0 + nl;
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
             const int pc = l16 + 16 * j;
@@ -449,7 +498,7 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(const DecodeArg
     for (int m = 0; m < NM; ++m) {
         const int rt = grp + 32 * m;
         const int rtc = rt < n_rt ? rt : 0;
-        const int s = rtc % K1;
+        const int s = rtc % k;
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < JP; ++j) {
@@ -471,8 +520,8 @@ __global__ __launch_bounds__(kDnThreads) void decode_down_kernel(const DecodeArg
         float y = 0.0f;
 #pragma unroll
         for (int s = 0; s < kMaxTopK; ++s)
-            if (s < k) y += wsc[s] * s_res[tid * K1 + s];
-        y += s_res[tid * K1 + k];
+            if (s < k) y += wsc[s] * s_res[tid * k + s];
+        y += ysh;
         a.y[(size_t)t * d + n0 + tid] = f32_to_bf16(y);
     }
 }
@@ -519,7 +568,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 g3(a.d / kDnOutRows, a.T);
-    const int n_rt = kDnOutRows * (a.k + 1);
+    const int n_rt = kDnOutRows * a.k;
     if (n_rt <= 32) launch_down<1>(a, g3, s);
     else if (n_rt <= 64) launch_down<2>(a, g3, s);
     else launch_down<3>(a, g3, s);

@@ -63,6 +63,7 @@ struct DecodeArgs {
     int32_t* sel_idx;    // [T][k]
     float* sel_w;        // [T][k]
     uint16_t* h;         // bf16 [T][k+1][I], slot k = the shared expert
+    float* y_sh;         // [T][d] the shared expert's down projection (fp32)
     uint16_t* y;         // bf16 [T][d]
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);

@@ -163,9 +163,11 @@ def test_workspace_bytes_cover_the_staged_buffers():
         # columns of a token, slots padded to MOE_MAX_TOPK)
         staged = 2 * (T * k * I + T * I + T * k * d) + T * (d // 32) * _abi.MOE_MAX_TOPK
         # decode region for up to MOE_MAX_DECODE_TOKENS tokens: router partial
-        # sums, logits, h of the k + 1 experts per token
+        # sums, logits, h of the k + 1 experts per token, the shared expert's
+        # fp32 down outputs
         nt = _abi.MOE_MAX_DECODE_TOKENS
-        dec = 4 * -(-d // _abi.MOE_DECODE_ROUTER_ROWS) * nt * E + 4 * nt * E + 2 * nt * (k + 1) * I
+        dec = (4 * -(-d // _abi.MOE_DECODE_ROUTER_ROWS) * nt * E + 4 * nt * E + 2 * nt * (k + 1) * I
+               + 4 * nt * d)
         assert staged + dec <= n <= staged + dec + 64 * 1024
     bad = _layer(d=100)
     assert lib.moe_workspace_bytes(C.addressof(bad), 16) == 0
