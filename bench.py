@@ -681,8 +681,9 @@ def bench_sweep(args, q4, torch, ev, stream):
 
 
 def bench_item_rows(args, q4, torch, ev, stream):
-    """Gate/up work-item height ablation: route + prefill at item heights 128, 64
-    and 32 rows (the rows that share one dequantised weight tile), T = 512, 2048,
+    """Gate/up work-item height ablation: route + prefill at item heights 128, 64,
+    32 and 16 rows (the rows that share one dequantised weight tile; 16-row items
+    fill half of one 32-row MFMA subtile), T = 512, 2048,
     4096, with the balanced router and with the skewed workload's router bias.
     Weights: the T=2048 workload's two sets, alternated; x: the first T rows of one
     seeded draw of 4096 rows; the skewed rows add the skewed workload's bias."""
@@ -710,7 +711,7 @@ def bench_item_rows(args, q4, torch, ev, stream):
             rec = {"T": T, "skew": skew}
             # two passes in opposite orders, the faster kept (clock ramps and
             # order effects cancel)
-            for m in (128, 64, 32, 32, 64, 128):
+            for m in (128, 64, 32, 16, 16, 32, 64, 128):
                 def step(i, tr=None):
                     q4.route(sets[skew][i % 2], xs, routing=r)
                     if tr is not None:
@@ -742,7 +743,7 @@ def bench_item_rows(args, q4, torch, ev, stream):
             rows.append(rec)
             log(f"item rows T={T} skew={skew}: " + ", ".join(
                 f"{m} rows {rec[f'rows{m}']['us_per_layer']:.1f} us/layer "
-                f"(gate/up {rec[f'rows{m}']['gate_up_us']:.1f})" for m in (128, 64, 32)))
+                f"(gate/up {rec[f'rows{m}']['gate_up_us']:.1f})" for m in (128, 64, 32, 16)))
             del r, y
     del sets, ws
     torch.cuda.empty_cache()

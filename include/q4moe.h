@@ -183,13 +183,15 @@ int moe_prefill(const moe_layer* L, const uint16_t* x, int32_t T, const moe_rout
    expert-sorted rows that share one on-chip dequantised weight tile
    ([Lily-M5] "Prefill: keep routing on the GPU, dequantize in flight" compares
    tile heights).  flags = 0: 128 rows (what moe_prefill uses);
-   MOE_ITEM_ROWS_64: 64 rows; MOE_ITEM_ROWS_32: 32 rows, one MFMA subtile.
-   Shorter items dequantise an expert's weights once per item instead of once
-   per 128 rows and pad less.  The result is the same whatever the height:
-   every row's sums are accumulated in the same order.  Both flags together, or
-   any other bit, is MOE_EINVAL. */
+   MOE_ITEM_ROWS_64: 64 rows; MOE_ITEM_ROWS_32: 32 rows, one MFMA subtile;
+   MOE_ITEM_ROWS_16: 16 rows, the upper half of one MFMA subtile (its other
+   16 rows are padding).  Shorter items dequantise an expert's weights once per
+   item instead of once per 128 rows and pad less.  The result is the same
+   whatever the height: every row's sums are accumulated in the same order.
+   More than one of these flags, or any other bit, is MOE_EINVAL. */
 #define MOE_ITEM_ROWS_64 2u
 #define MOE_ITEM_ROWS_32 4u
+#define MOE_ITEM_ROWS_16 8u
 int moe_prefill_ex(const moe_layer* L, const uint16_t* x, int32_t T, const moe_routing* r,
                    void* ws, size_t ws_bytes, uint16_t* y, uint32_t flags, void* stream);
 

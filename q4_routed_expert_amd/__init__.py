@@ -156,16 +156,17 @@ def route(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting | None = N
     return r
 
 
-_ITEM_ROWS_FLAGS = {128: 0, 64: _abi.MOE_ITEM_ROWS_64, 32: _abi.MOE_ITEM_ROWS_32}
+_ITEM_ROWS_FLAGS = {128: 0, 64: _abi.MOE_ITEM_ROWS_64, 32: _abi.MOE_ITEM_ROWS_32,
+                    16: _abi.MOE_ITEM_ROWS_16}
 
 
 def prefill(layer: DeviceLayer, x: torch.Tensor, routing: DeviceRouting,
             ws: torch.Tensor | None = None, y: torch.Tensor | None = None,
             stream=None, item_rows: int = 128) -> torch.Tensor:
     """moe_prefill (item_rows = 128) or moe_prefill_ex with the gate/up work-item
-    height item_rows (64 or 32)."""
+    height item_rows (64, 32 or 16)."""
     if item_rows not in _ITEM_ROWS_FLAGS:
-        raise ValueError(f"item_rows must be one of 128, 64, 32, not {item_rows}")
+        raise ValueError(f"item_rows must be one of 128, 64, 32, 16, not {item_rows}")
     T = x.shape[0]
     if ws is None:
         ws = workspace(layer, T, x.device)

@@ -8,7 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq4moe.so
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_LOGITS_IN = 1
-MOE_ITEM_ROWS_64, MOE_ITEM_ROWS_32 = 2, 4
+MOE_ITEM_ROWS_64, MOE_ITEM_ROWS_32, MOE_ITEM_ROWS_16 = 2, 4, 8
 MOE_BLOCK_ROWS = 32
 MOE_TILE_ROWS = 128
 MOE_ROUTE_BLOCK = 256

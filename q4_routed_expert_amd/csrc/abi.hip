@@ -219,8 +219,8 @@ int moe_prefill_ex(const moe_layer* L, const uint16_t* x, int32_t T, const moe_r
     if ((rc = check_layer(L)) || (rc = check_tokens(T)) || (rc = check_routing(r)) ||
         (rc = check_ptr(x, "x")) || (rc = check_ptr(y, "y")) || (rc = check_ptr(ws, "workspace")))
         return rc;
-    if ((flags & ~(MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32)) ||
-        (flags & (MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32)) == (MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32))
+    const uint32_t rows_flags = MOE_ITEM_ROWS_64 | MOE_ITEM_ROWS_32 | MOE_ITEM_ROWS_16;
+    if ((flags & ~rows_flags) || __builtin_popcount(flags & rows_flags) > 1)
         return fail(MOE_EINVAL, "prefill flags 0x%x", flags);
     const size_t need = moe_workspace_bytes(L, T);
     if (ws_bytes < need)
@@ -246,7 +246,10 @@ int moe_prefill_ex(const moe_layer* L, const uint16_t* x, int32_t T, const moe_r
     a.n_tiles = r->n_tiles;
     a.topk_w = r->topk_w;
     a.tile_bound = moe_block_map_capacity(T, L->top_k, L->n_experts, MOE_TILE_ROWS);
-    a.item_sh = (flags & MOE_ITEM_ROWS_32) ? 2 : (flags & MOE_ITEM_ROWS_64) ? 1 : 0;
+    a.item_sh = (flags & MOE_ITEM_ROWS_16)   ? 3
+                : (flags & MOE_ITEM_ROWS_32) ? 2
+                : (flags & MOE_ITEM_ROWS_64) ? 1
+                                             : 0;
     a.h = (uint16_t*)(base + pw.h);
     a.h_sh = (uint16_t*)(base + pw.h_sh);
     a.part = (uint16_t*)(base + pw.part);

@@ -36,7 +36,7 @@ struct PrefillArgs {
     const int32_t* n_tiles;
     const float* topk_w;
     int tile_bound;      // host upper bound on *n_tiles
-    int item_sh;         // gate/up work items are 128 >> item_sh rows (0, 1 or 2)
+    int item_sh;         // gate/up work items are 128 >> item_sh rows (0 .. 3)
     uint16_t* h;         // bf16 [T*k][I], expert-sorted rows
     uint16_t* h_sh;      // bf16 [T][I]
     uint16_t* part;      // fp16 [T*k][d], routed expert outputs scaled by 2^-pexp, rows in

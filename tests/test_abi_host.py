@@ -37,7 +37,7 @@ def test_header_limits_match_binding():
     for name in ("MOE_GROUP", "MOE_MAX_EXPERTS", "MOE_MAX_TOPK", "MOE_MAX_TOKENS", "MOE_MAX_D",
                  "MOE_MAX_INTER", "MOE_BLOCK_ROWS", "MOE_TILE_ROWS", "MOE_ROUTE_BLOCK",
                  "MOE_DECODE_ROUTER_ROWS", "MOE_MAX_DECODE_TOKENS", "MOE_LOGITS_IN",
-                 "MOE_MAX_VOCAB", "MOE_ITEM_ROWS_64", "MOE_ITEM_ROWS_32"):
+                 "MOE_MAX_VOCAB", "MOE_ITEM_ROWS_64", "MOE_ITEM_ROWS_32", "MOE_ITEM_ROWS_16"):
         m = re.search(rf"#define {name} (\d+)", text)
         assert m, name
         if hasattr(_abi, name):
@@ -123,11 +123,15 @@ def test_prefill_ex_checks_flags_before_launch():
     r = _routing()
     call = lambda flags, ws=need: lib.moe_prefill_ex(C.addressof(L), FAKE, 2048, C.addressof(r),
                                                      FAKE, ws, FAKE, flags, None)
-    assert call(_abi.MOE_ITEM_ROWS_64 | _abi.MOE_ITEM_ROWS_32) == _abi.MOE_EINVAL
+    rows = (_abi.MOE_ITEM_ROWS_64, _abi.MOE_ITEM_ROWS_32, _abi.MOE_ITEM_ROWS_16)
+    for i, f in enumerate(rows):  # any two heights together
+        for g in rows[i + 1:]:
+            assert call(f | g) == _abi.MOE_EINVAL
+    assert call(rows[0] | rows[1] | rows[2]) == _abi.MOE_EINVAL
     assert call(1) == _abi.MOE_EINVAL
-    assert call(8) == _abi.MOE_EINVAL
+    assert call(16) == _abi.MOE_EINVAL
     # valid flags get as far as the workspace check
-    for flags in (0, _abi.MOE_ITEM_ROWS_64, _abi.MOE_ITEM_ROWS_32):
+    for flags in (0,) + rows:
         assert call(flags, need - 1) == _abi.MOE_EWORKSPACE
 
 

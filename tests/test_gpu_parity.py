@@ -360,7 +360,7 @@ def test_gate_up_round_robin_schedule(dev):
                                          # schedule takes: the round-robin unit list
 ])
 def test_item_rows_variants(T, d, inter, E, k, bias, seed, dev):
-    # the gate/up work item at 64 and 32 rows: every row's products are
+    # the gate/up work item at 64, 32 and 16 rows: every row's products are
     # accumulated in the same order as at 128 rows, so y is bit-identical; the
     # 32-row run is also compared with the oracle
     rng = np.random.default_rng(2000 + seed)
@@ -376,9 +376,9 @@ def test_item_rows_variants(T, d, inter, E, k, bias, seed, dev):
     compare_routing(r, ref, T, E, k, bm, tm)
     n_items32 = 4 * int(r.n_tiles.cpu()[0]) + (T + 63) // 64
     ws = q4.workspace(layer, T, dev)
-    ys = {m: host_bits(q4.prefill(layer, xd, r, ws, item_rows=m)) for m in (128, 64, 32)}
+    ys = {m: host_bits(q4.prefill(layer, xd, r, ws, item_rows=m)) for m in (128, 64, 32, 16)}
     torch.cuda.synchronize()
-    for m in (64, 32):
+    for m in (64, 32, 16):
         assert np.array_equal(ys[m], ys[128]), f"item_rows={m} differs from 128"
     tokens = np.arange(T, dtype=np.int32) if T <= 600 else item_tokens(ref, T, k)
     y_exact, _ = oracle.layer_tokens(L, x, tokens, ref["idx"], ref["w"])
@@ -387,7 +387,7 @@ def test_item_rows_variants(T, d, inter, E, k, bias, seed, dev):
         f"err/rms={err:.3e}, worst err/allowed={worst:.3f} ({len(tokens)} tokens)")
     assert worst <= 1.0
     with pytest.raises(ValueError):
-        q4.prefill(layer, xd, r, ws, item_rows=16)
+        q4.prefill(layer, xd, r, ws, item_rows=48)
 
 
 def test_prefill_at_the_token_limit(dev):
